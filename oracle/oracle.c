@@ -1,0 +1,268 @@
+/*
+ * oracle.c -- plain, serial CPU reference for prefix scan and stream compaction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or calls
+ * this file; only the test-suite, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no source, header, table or constant with the HIP library.
+ *
+ * Every routine is the textbook definition, evaluated one element after another,
+ * in the order the definition states.  No blocking, no reordering, no vectorised
+ * tricks: a reader can check each loop against the definitions by eye.
+ *
+ * Citations name the source page and its section:
+ *   [Scan3]  geek-doc.cn, "并行前缀和 scan: Hillis-Steele、Blelloch 与 warp shuffle
+ *            三种写法" (parallel prefix scan, three ways); sections 一..五 and the
+ *            pitfall list ("常见坑").
+ *   [Blog2]  lpnh.cn/news/2866224, parallel scan / prefix sum overview; sections 1..7.
+ *   [SIMT3]  pgsm.cn/news/414823, "SIMT数据依赖与并行前缀和：从原理到流压缩实战";
+ *            sections 1..5.
+ *
+ * Codes used below (defined here, independently of the library's header):
+ *   dtype: 0 = int32, 1 = uint32, 2 = float32
+ *   op:    0 = sum,   1 = max,    2 = xor
+ *   cmp:   0 = <, 1 = <=, 2 = >, 3 = >=, 4 = ==, 5 = !=
+ * Readings of points the pages leave open (operator identities, integer wrap,
+ * tie rule of the float max) are stated at each routine.
+ */
+#include <stdint.h>
+#include <string.h>
+
+#define OR_INT32 0
+#define OR_UINT32 1
+#define OR_FLOAT32 2
+
+#define OR_SUM 0
+#define OR_MAX 1
+#define OR_XOR 2
+
+/* ---- the binary operators ------------------------------------------------
+ * [Scan3] §一 (last paragraph) and §三: scan is defined for any associative
+ * operator; the default is addition, and max and xor are named examples.
+ * Integer addition wraps modulo 2^32 (two's complement), computed on uint32_t so
+ * that C has no undefined behaviour; the pages never overflow, so any wrapping
+ * rule agrees with them, and this one is what 32-bit hardware addition does. */
+static uint32_t op_u32(int dtype, int op, uint32_t a, uint32_t b)
+{
+    switch (op) {
+    case OR_SUM:
+        return a + b; /* wraps mod 2^32 */
+    case OR_XOR:
+        return a ^ b;
+    case OR_MAX:
+        if (dtype == OR_INT32)
+            return ((int32_t)a > (int32_t)b) ? a : b;
+        return (a > b) ? a : b;
+    }
+    return 0;
+}
+
+/* Identity of each operator: the value an exclusive scan puts in its first cell.
+ * [Scan3] §一 fixes z[0] = 0 for addition; for max and xor the same role is
+ * played by the operator's identity (0 for xor, the smallest value for max). */
+static uint32_t identity_u32(int dtype, int op)
+{
+    if (op == OR_MAX)
+        return dtype == OR_INT32 ? 0x80000000u : 0u;
+    return 0u;
+}
+
+/* ---- integer scans (int32 / uint32; sum, max, xor) -------------------------
+ * Inclusive: y[i] = x[0] (+) ... (+) x[i]            [Scan3] §一, first formula
+ * Exclusive: z[0] = identity, z[i] = x[0] (+) ... (+) x[i-1]   [Scan3] §一
+ * Serial evaluation: one accumulator carried left to right, exactly the serial
+ * loop of [Scan3] §一 and [Blog2] §2.1.  The total (the value no exclusive cell
+ * holds, [Scan3] §一) is written to *total when total != NULL.
+ * Returns 0, or -1 on an unknown code. */
+int oracle_scan_u32(const uint32_t *x, uint32_t *y, int64_t n, int dtype, int op,
+                    int inclusive, uint32_t *total)
+{
+    if ((dtype != OR_INT32 && dtype != OR_UINT32) || op < OR_SUM || op > OR_XOR)
+        return -1;
+    uint32_t acc = identity_u32(dtype, op);
+    if (inclusive) {
+        /* y[0] = x[0]; y[i] = y[i-1] (+) x[i] */
+        for (int64_t i = 0; i < n; ++i) {
+            acc = (i == 0) ? x[0] : op_u32(dtype, op, acc, x[i]);
+            y[i] = acc;
+        }
+    } else {
+        /* z[0] = identity; z[i] = z[i-1] (+) x[i-1] */
+        for (int64_t i = 0; i < n; ++i) {
+            y[i] = acc;
+            acc = op_u32(dtype, op, acc, x[i]);
+        }
+    }
+    if (total)
+        *total = acc;
+    return 0;
+}
+
+/* ---- float32 sum, accumulated in double ------------------------------------
+ * Same definition as above with real addition.  The accumulator is a double, so
+ * the result is the exact prefix up to double rounding.  bound[i] receives
+ * sum_{j<=i} |x[j]| (also in double; for the exclusive scan too, i.e. the bound
+ * includes x[i]) -- the scale of the float32 tolerance that a parallel order of
+ * additions must meet ([Scan3] pitfall list: float addition is not associative,
+ * so a parallel result may differ in the last bits).  bound may be NULL. */
+void oracle_scan_f32_sum(const float *x, double *y, double *bound, int64_t n, int inclusive,
+                         double *total)
+{
+    double acc = 0.0;
+    double mag = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)x[i];
+        mag += (v < 0.0) ? -v : v;
+        if (inclusive) {
+            acc = (i == 0) ? v : acc + v;
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc += v;
+        }
+        if (bound)
+            bound[i] = mag;
+    }
+    if (total)
+        *total = acc;
+}
+
+/* ---- float32 max ------------------------------------------------------------
+ * max(a, b) = (a > b) ? a : b, evaluated in float32.  On a tie (equal values,
+ * including -0 against +0) it keeps the right operand, so a prefix holds the
+ * right-most of its largest elements; this rule is associative for non-NaN data,
+ * hence any association order yields the same bits.  Identity: -infinity.
+ * NaN inputs are outside the defined domain. */
+static float fmax_right(float a, float b)
+{
+    return (a > b) ? a : b;
+}
+
+void oracle_scan_f32_max(const float *x, float *y, int64_t n, int inclusive, float *total)
+{
+    uint32_t ninf_bits = 0xff800000u;
+    float acc;
+    memcpy(&acc, &ninf_bits, sizeof acc);
+    for (int64_t i = 0; i < n; ++i) {
+        if (inclusive) {
+            acc = (i == 0) ? x[0] : fmax_right(acc, x[i]);
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc = fmax_right(acc, x[i]);
+        }
+    }
+    if (total)
+        *total = acc;
+}
+
+/* ---- the compaction predicate ----------------------------------------------
+ * element (cmp) threshold, compared in the element's own type: signed for int32,
+ * unsigned for uint32, IEEE float comparison (C semantics) for float32. */
+static int pred_holds(int dtype, int cmp, uint32_t vbits, uint32_t tbits)
+{
+    int lt, eq;
+    if (dtype == OR_FLOAT32) {
+        float v, t;
+        memcpy(&v, &vbits, sizeof v);
+        memcpy(&t, &tbits, sizeof t);
+        switch (cmp) {
+        case 0: return v < t;
+        case 1: return v <= t;
+        case 2: return v > t;
+        case 3: return v >= t;
+        case 4: return v == t;
+        case 5: return v != t;
+        }
+        return 0;
+    }
+    if (dtype == OR_INT32) {
+        lt = (int32_t)vbits < (int32_t)tbits;
+    } else {
+        lt = vbits < tbits;
+    }
+    eq = vbits == tbits;
+    switch (cmp) {
+    case 0: return lt;
+    case 1: return lt || eq;
+    case 2: return !lt && !eq;
+    case 3: return !lt;
+    case 4: return eq;
+    case 5: return !eq;
+    }
+    return 0;
+}
+
+/* ---- stream compaction, serial form -----------------------------------------
+ * Keep, in input order, every element whose predicate holds; return how many
+ * were kept.  [Scan3] §一 (the 8-element compaction example) and [SIMT3] §4.1
+ * (inputs copied to the front of the output, in order, plus a count).
+ * out must hold n elements; cells at and beyond the count are not written.
+ * Returns the count, or -1 on an unknown code. */
+int64_t oracle_compact(const uint32_t *x, uint32_t *out, int64_t n, int dtype, int cmp,
+                       uint32_t thr_bits)
+{
+    if (dtype < OR_INT32 || dtype > OR_FLOAT32 || cmp < 0 || cmp > 5)
+        return -1;
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (pred_holds(dtype, cmp, x[i], thr_bits))
+            out[c++] = x[i];
+    }
+    return c;
+}
+
+/* ---- stream compaction, flag / exclusive-scan / scatter form ----------------
+ * The three steps of [Scan3] §一 and [SIMT3] §4.2: (1) flag[i] = 1 if the
+ * predicate holds, else 0; (2) exclusive sum scan of the flags gives each kept
+ * element its output index; (3) every kept element writes out[index[i]] = x[i];
+ * the count is index[n-1] + flag[n-1].  Computed with its own arrays so that it
+ * is an independent check of the serial form above.  flags and index are caller
+ * scratch of n elements each.  Returns the count, or -1 on an unknown code. */
+int64_t oracle_compact_via_scan(const uint32_t *x, uint32_t *out, int64_t n, int dtype, int cmp,
+                                uint32_t thr_bits, int64_t *flags, int64_t *index)
+{
+    if (dtype < OR_INT32 || dtype > OR_FLOAT32 || cmp < 0 || cmp > 5)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        flags[i] = pred_holds(dtype, cmp, x[i], thr_bits) ? 1 : 0;
+    int64_t run = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        index[i] = run;
+        run += flags[i];
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        if (flags[i])
+            out[index[i]] = x[i];
+    }
+    return n > 0 ? index[n - 1] + flags[n - 1] : 0;
+}
+
+/* ---- batched row scan -------------------------------------------------------
+ * rows x cols, row-major and contiguous; each row is scanned on its own, with no
+ * carry from one row into the next: the single-array definition applied to every
+ * row.  This is the uniform-length case of the segmented scan that [Blog2] §7.2
+ * mentions.  For float32 sum, y/bound are double arrays of rows*cols. */
+int oracle_batched_u32(const uint32_t *x, uint32_t *y, int64_t rows, int64_t cols, int dtype,
+                       int op, int inclusive)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        int rc = oracle_scan_u32(x + r * cols, y + r * cols, cols, dtype, op, inclusive, 0);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+void oracle_batched_f32_sum(const float *x, double *y, double *bound, int64_t rows, int64_t cols,
+                            int inclusive)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        oracle_scan_f32_sum(x + r * cols, y + r * cols, bound ? bound + r * cols : 0, cols,
+                            inclusive, 0);
+}
+
+void oracle_batched_f32_max(const float *x, float *y, int64_t rows, int64_t cols, int inclusive)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        oracle_scan_f32_max(x + r * cols, y + r * cols, cols, inclusive, 0);
+}

@@ -1,0 +1,310 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with something other than itself: values the pages print (fixtures under
+tests/golden/, each with its citation), closed forms, invariants, numpy library
+routines that reduce to the same definition, and brute force over tiny inputs.
+They are written as plain functions so the same list can be run against copies of
+the oracle with a planted mistake (tests/test_oracle_mutants.py).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+from conftest import load_golden
+from oracle import brute
+
+INT_DTYPES = ("int32", "uint32")
+OPS = ("sum", "max", "xor")
+M32 = 0xFFFFFFFF
+
+
+def _bits(a):
+    return [int(v) & M32 for v in np.asarray(a).view(np.uint32).tolist()]
+
+
+def _ident(dtype, op):
+    return brute.identity(dtype, op)
+
+
+# ---------------------------------------------------------------- page values
+
+def pin_worked_example_scan(orc):
+    g = load_golden("worked_example.txt")
+    x = np.array(g["x"], np.int32)
+    inc = orc.scan(x, "sum", True)
+    exc = orc.scan(x, "sum", False)
+    assert inc.y.tolist() == g["inclusive"]
+    assert exc.y.tolist() == g["exclusive"]
+    assert int(inc.total) == g["total"][0] and int(exc.total) == g["total"][0]
+    # the same example through the float path (exact: small integers)
+    xf = x.astype(np.float32)
+    fi = orc.scan(xf, "sum", True)
+    fe = orc.scan(xf, "sum", False)
+    assert fi.y.tolist() == [float(v) for v in g["inclusive"]]
+    assert fe.y.tolist() == [float(v) for v in g["exclusive"]]
+    # and as uint32
+    assert orc.scan(x.view(np.uint32), "sum", False).y.tolist() == g["exclusive"]
+
+
+def pin_worked_example_compaction(orc):
+    g = load_golden("worked_example.txt")
+    x = np.array(g["x"], np.int32)
+    cmp, thr = g["predicate"][0], g["predicate"][1]
+    for via in (False, True):
+        out, count = orc.compact(x, cmp, thr, via_scan=via)
+        assert out.tolist() == g["compacted"]
+        assert count == g["count"][0]
+    # the flags and their exclusive scan, as printed
+    flags = np.array([1 if v > thr else 0 for v in g["x"]], np.int32)
+    assert flags.tolist() == g["flags"]
+    assert orc.scan(flags, "sum", False).y.tolist() == g["flags_exclusive"]
+
+
+def pin_two_block_decomposition(orc):
+    g = load_golden("two_block.txt")
+    x = np.array(g["x"], np.int32)
+    b = g["block_size"][0]
+    blocks = [x[i:i + b] for i in range(0, len(x), b)]
+    totals = [int(orc.scan(blk, "sum", True).total) for blk in blocks]
+    assert totals == g["block_totals"]
+    offsets = orc.scan(np.array(totals, np.int32), "sum", False).y.tolist()
+    assert offsets == g["block_offsets"]
+    local = orc.scan(blocks[1], "sum", False).y
+    assert local.tolist() == g["block1_local_exclusive"]
+    glob = (local + offsets[1]).tolist()
+    assert glob == g["block1_global_exclusive"]
+    assert orc.scan(x, "sum", False).y[b:].tolist() == glob
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_inclusive_exclusive_relation(orc):
+    """z[0] = identity, z[i] = y[i-1], total = y[n-1] = z[n-1] (+) x[n-1]."""
+    rng = np.random.default_rng(11)
+    for dtype in INT_DTYPES:
+        for op in OPS:
+            for n in (1, 2, 7, 100):
+                x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+                x = x.view(np.int32) if dtype == "int32" else x
+                inc = orc.scan(x, op, True)
+                exc = orc.scan(x, op, False)
+                yb, zb = _bits(inc.y), _bits(exc.y)
+                assert zb[0] == _ident(dtype, op)
+                assert zb[1:] == yb[:-1]
+                f = brute.op_fn(dtype, op)
+                tb = int(np.array([inc.total]).view(np.uint32)[0])
+                assert tb == yb[-1] == f(zb[-1], _bits(x)[-1])
+                assert int(np.array([exc.total]).view(np.uint32)[0]) == tb
+
+
+def pin_empty_input(orc):
+    for dtype in INT_DTYPES + ("float32",):
+        for op in OPS:
+            if dtype == "float32" and op == "xor":
+                continue
+            x = np.zeros(0, dtype)
+            for inc in (True, False):
+                r = orc.scan(x, op, inc)
+                assert r.y.size == 0
+                if dtype != "float32":
+                    assert int(np.array([r.total]).view(np.uint32)[0]) == _ident(dtype, op)
+    out, c = orc.compact(np.zeros(0, np.int32), "lt", 5)
+    assert c == 0 and out.size == 0
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_closed_forms_sum(orc):
+    n = 100_003  # n(n+1)/2 > 2^32: exercises the mod-2^32 wrap
+    ones = np.ones(n, np.int32)
+    assert np.array_equal(orc.scan(ones, "sum", True).y, np.arange(1, n + 1, dtype=np.int32))
+    assert np.array_equal(orc.scan(ones, "sum", False).y, np.arange(0, n, dtype=np.int32))
+    iota = np.arange(n, dtype=np.uint32)
+    i = np.arange(n, dtype=np.uint64)
+    want = ((i * (i + 1) // 2) & M32).astype(np.uint32)
+    assert np.array_equal(orc.scan(iota, "sum", True).y, want)
+    assert np.array_equal(orc.scan(iota.view(np.int32), "sum", True).y.view(np.uint32), want)
+    # exclusive of iota: i(i-1)/2
+    want_e = ((i * (i - 1) // 2) & M32).astype(np.uint32)
+    want_e[0] = 0
+    assert np.array_equal(orc.scan(iota, "sum", False).y, want_e)
+
+
+def pin_closed_forms_xor(orc):
+    """xor of 0..k is k, 1, k+1, 0 for k mod 4 = 0, 1, 2, 3."""
+    n = 5000
+    iota = np.arange(n, dtype=np.uint32)
+    y = orc.scan(iota, "xor", True).y.tolist()
+    for k in range(n):
+        assert y[k] == [k, 1, k + 1, 0][k % 4]
+    # self-inverse: x xor-scanned twice from a shifted copy recovers x
+    z = orc.scan(iota, "xor", False).y
+    assert np.array_equal(z ^ orc.scan(iota, "xor", True).y, iota)
+
+
+def pin_closed_forms_max(orc):
+    asc = np.arange(-500, 500, dtype=np.int32)
+    assert np.array_equal(orc.scan(asc, "max", True).y, asc)
+    desc = asc[::-1].copy()
+    assert np.array_equal(orc.scan(desc, "max", True).y, np.full_like(desc, desc[0]))
+    e = orc.scan(desc, "max", False).y
+    assert int(e[0]) == -(1 << 31) and np.all(e[1:] == desc[0])
+    # signed vs unsigned: 0xFFFFFFFF is -1 as int32 but the largest uint32
+    x = np.array([5, -1, 3], np.int32)
+    assert orc.scan(x, "max", True).y.tolist() == [5, 5, 5]
+    assert orc.scan(x.view(np.uint32), "max", True).y.tolist() == [5, 0xFFFFFFFF, 0xFFFFFFFF]
+    # float max: ascending / descending, exclusive starts at -inf
+    f = np.linspace(-3, 3, 101).astype(np.float32)
+    assert np.array_equal(orc.scan(f, "max", True).y, f)
+    fd = f[::-1].copy()
+    assert np.array_equal(orc.scan(fd, "max", True).y, np.full_like(fd, fd[0]))
+    fe = orc.scan(fd, "max", False).y
+    assert np.isneginf(fe[0]) and np.all(fe[1:] == fd[0])
+
+
+def pin_float_max_tie_rule(orc):
+    """Ties keep the right operand: the prefix carries the bits of the right-most of
+    its largest elements (seen through +0 / -0)."""
+    x = np.array([0.0, -0.0, 1.0, -0.0, 0.0, -0.0], np.float32)
+    y = orc.scan(x, "max", True).y
+    assert _bits(y) == _bits(np.array([0.0, -0.0, 1.0, 1.0, 1.0, 1.0], np.float32))
+    x2 = np.array([-0.0, 0.0, -0.0], np.float32)
+    assert _bits(orc.scan(x2, "max", True).y) == _bits(x2)
+
+
+# ---------------------------------------------------------------- library routines
+
+def pin_numpy_cumulative(orc):
+    rng = np.random.default_rng(7)
+    n = 20_000
+    xi = rng.integers(-(1 << 31), 1 << 31, n, dtype=np.int64).astype(np.int32)
+    xu = xi.view(np.uint32)
+    cs = (np.cumsum(xu.astype(np.uint64)) & M32).astype(np.uint32)
+    assert np.array_equal(orc.scan(xi, "sum", True).y.view(np.uint32), cs)
+    assert np.array_equal(orc.scan(xu, "sum", True).y, cs)
+    assert np.array_equal(orc.scan(xi, "max", True).y, np.maximum.accumulate(xi))
+    assert np.array_equal(orc.scan(xu, "max", True).y, np.maximum.accumulate(xu))
+    assert np.array_equal(orc.scan(xu, "xor", True).y, np.bitwise_xor.accumulate(xu))
+    xf = (rng.standard_normal(n) * 100).astype(np.float32)
+    assert np.array_equal(orc.scan(xf, "max", True).y, np.maximum.accumulate(xf))
+
+
+def pin_fp32_sum_exact_and_fsum(orc):
+    """Integer-valued float32 data with partial sums < 2^24 is summed exactly in any
+    order; general float data matches correctly rounded prefix sums (math.fsum)."""
+    rng = np.random.default_rng(5)
+    xi = rng.integers(-50, 50, 3000).astype(np.float32)
+    inc = orc.scan(xi, "sum", True)
+    exc = orc.scan(xi, "sum", False)
+    ci = np.cumsum(xi.astype(np.int64))
+    assert np.array_equal(inc.y, ci.astype(np.float64))
+    assert exc.y[0] == 0.0 and np.array_equal(exc.y[1:], ci[:-1].astype(np.float64))
+    assert np.array_equal(inc.bound, np.cumsum(np.abs(xi.astype(np.int64))).astype(np.float64))
+    assert np.array_equal(exc.bound, inc.bound)
+    assert inc.total == exc.total == float(ci[-1])
+    xf = (rng.random(300) * 2 - 1).astype(np.float32)
+    vals = [float(v) for v in xf]
+    fi = brute.fsum_inclusive(vals)
+    fe = brute.fsum_exclusive(vals)
+    ri = orc.scan(xf, "sum", True).y
+    re = orc.scan(xf, "sum", False).y
+    for k in range(len(vals)):
+        assert abs(ri[k] - fi[k]) <= 1e-12 * (1 + abs(fi[k]))
+        assert abs(re[k] - fe[k]) <= 1e-12 * (1 + abs(fe[k]))
+    assert np.allclose(orc.scan(xf, "sum", True).bound,
+                       np.cumsum(np.abs(xf.astype(np.float64))), rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------- brute force
+
+def pin_brute_force_random(orc):
+    rng = np.random.default_rng(3)
+    for dtype in INT_DTYPES:
+        for op in OPS:
+            for n in list(range(1, 17)) + [31, 64]:
+                x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+                if op == "sum" and rng.random() < 0.5:
+                    x = rng.integers(0, 10, n).astype(np.uint32)
+                x = x.view(np.int32) if dtype == "int32" else x
+                b = _bits(x)
+                assert _bits(orc.scan(x, op, True).y) == brute.inclusive_bits(b, dtype, op)
+                assert _bits(orc.scan(x, op, False).y) == brute.exclusive_bits(b, dtype, op)
+
+
+def pin_brute_force_exhaustive_tiny(orc):
+    alphabet = [0, 1, 2, 0x7FFFFFFF, 0x80000000, 0xFFFFFFFF]
+    for dtype in INT_DTYPES:
+        for op in OPS:
+            for n in range(1, 5):
+                for combo in itertools.product(alphabet, repeat=n):
+                    x = np.array(combo, np.uint32)
+                    x = x.view(np.int32) if dtype == "int32" else x
+                    b = list(combo)
+                    assert _bits(orc.scan(x, op, True).y) == brute.inclusive_bits(b, dtype, op)
+                    assert _bits(orc.scan(x, op, False).y) == brute.exclusive_bits(b, dtype, op)
+
+
+def pin_compaction_brute_and_numpy(orc):
+    rng = np.random.default_rng(9)
+    cmps = ("lt", "le", "gt", "ge", "eq", "ne")
+    for dtype in ("int32", "uint32", "float32"):
+        for n in (1, 5, 17, 64, 1000):
+            if dtype == "float32":
+                x = rng.integers(-4, 5, n).astype(np.float32)
+                thr = np.float32(1.0)
+            elif dtype == "int32":
+                x = rng.integers(-4, 5, n).astype(np.int32)
+                thr = np.int32(1)
+            else:
+                x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+                x[::3] = 0x7FFFFFFF
+                thr = np.uint32(0x7FFFFFFF)
+            vals = x.tolist()
+            for cmp in cmps:
+                want, wc = brute.compact_values(vals, cmp, thr.item())
+                for via in (False, True):
+                    out, c = orc.compact(x, cmp, thr, via_scan=via)
+                    assert c == wc and out.tolist() == want
+    # numpy boolean mask at a larger size, selectivities 0, 50 %, 100 %
+    x = rng.integers(0, 1 << 31, 200_000, dtype=np.int64).astype(np.int32)
+    for thr in (0, 1 << 30, (1 << 31) - 1):
+        out, c = orc.compact(x, "lt", thr)
+        want = x[x < thr]
+        assert c == want.size and np.array_equal(out, want)
+    out, c = orc.compact(x, "ge", 0)  # everything kept: an exact copy
+    assert c == x.size and np.array_equal(out, x)
+    # stability of the payload bits: -0.0 and +0.0 are equal under ==, both kept in order
+    xz = np.array([0.0, -0.0, 1.0, -0.0], np.float32)
+    out, c = orc.compact(xz, "eq", np.float32(0.0))
+    assert c == 3 and _bits(out) == _bits(np.array([0.0, -0.0, -0.0], np.float32))
+    # NaN is unordered: never < or ==, always !=
+    xn = np.array([np.nan, 1.0, np.nan], np.float32)
+    assert orc.compact(xn, "lt", np.float32(5.0))[1] == 1
+    assert orc.compact(xn, "ne", np.float32(1.0))[1] == 2
+
+
+def pin_batched_rows(orc):
+    rng = np.random.default_rng(13)
+    x = rng.integers(0, 10, (37, 64)).astype(np.int32)
+    y = orc.batched(x, "sum", False).y
+    want = np.cumsum(x, axis=1) - x
+    assert np.array_equal(y, want.astype(np.int32))
+    assert np.all(y[:, 0] == 0)  # no carry from the previous row
+    yi = orc.batched(x, "sum", True).y
+    assert np.array_equal(yi, np.cumsum(x, axis=1).astype(np.int32))
+    xm = rng.integers(-100, 100, (9, 33)).astype(np.int32)
+    assert np.array_equal(orc.batched(xm, "max", True).y, np.maximum.accumulate(xm, axis=1))
+    xf = rng.random((5, 64)).astype(np.float32)
+    r = orc.batched(xf, "sum", False)
+    for row in range(5):
+        fe = brute.fsum_exclusive([float(v) for v in xf[row]])
+        assert max(abs(a - b) for a, b in zip(r.y[row], fe)) <= 1e-12
+        assert r.y[row, 0] == 0.0
+    assert np.allclose(r.bound, np.cumsum(xf.astype(np.float64), axis=1), rtol=1e-14)
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

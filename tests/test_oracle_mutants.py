@@ -1,0 +1,57 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that the
+pins catch every one: a dropped term, a wrong sign or index, a swapped operand,
+the inclusive/exclusive mix-up, a wrong identity, a signed/unsigned slip."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+# (name, text in oracle.c, replacement); each text must occur exactly once.
+MUTANTS = [
+    ("exclusive_becomes_inclusive",
+     "            y[i] = acc;\n            acc = op_u32(dtype, op, acc, x[i]);",
+     "            acc = op_u32(dtype, op, acc, x[i]);\n            y[i] = acc;"),
+    ("inclusive_wrong_index",
+     "acc = (i == 0) ? x[0] : op_u32(dtype, op, acc, x[i]);",
+     "acc = (i == 0) ? x[0] : op_u32(dtype, op, acc, x[i - 1]);"),
+    ("sum_sign", "return a + b; /* wraps mod 2^32 */", "return a - b;"),
+    ("xor_is_or", "return a ^ b;", "return a | b;"),
+    ("max_identity_zero", "return dtype == OR_INT32 ? 0x80000000u : 0u;", "return 0u;"),
+    ("int32_max_unsigned", "return ((int32_t)a > (int32_t)b) ? a : b;", "return (a > b) ? a : b;"),
+    ("uint32_max_signed", "        return (a > b) ? a : b;\n    }",
+     "        return ((int32_t)a > (int32_t)b) ? a : b;\n    }"),
+    ("f32_sum_sign", "acc = (i == 0) ? v : acc + v;", "acc = (i == 0) ? v : acc - v;"),
+    ("f32_exclusive_dropped_term", "            y[i] = acc;\n            acc += v;",
+     "            y[i] = acc;\n            acc = v;"),
+    ("f32_bound_not_abs", "mag += (v < 0.0) ? -v : v;", "mag += v;"),
+    ("f32_max_tie_left", "    return (a > b) ? a : b;\n}", "    return (a >= b) ? a : b;\n}"),
+    ("f32_max_identity_zero", "uint32_t ninf_bits = 0xff800000u;", "uint32_t ninf_bits = 0u;"),
+    ("compact_negated", "        if (pred_holds(dtype, cmp, x[i], thr_bits))\n            out[c++] = x[i];",
+     "        if (!pred_holds(dtype, cmp, x[i], thr_bits))\n            out[c++] = x[i];"),
+    ("compact_inclusive_index", "        index[i] = run;\n        run += flags[i];",
+     "        run += flags[i];\n        index[i] = run;"),
+    ("pred_lt_is_le", "    case 0: return lt;", "    case 0: return lt || eq;"),
+    ("pred_int32_unsigned", "lt = (int32_t)vbits < (int32_t)tbits;", "lt = vbits < tbits;"),
+    ("pred_float_gt_ge", "        case 2: return v > t;", "        case 2: return v >= t;"),
+    ("batched_row_stride", "oracle_scan_u32(x + r * cols, y + r * cols,",
+     "oracle_scan_u32(x + r, y + r * cols,"),
+    ("batched_f32_carry", "oracle_scan_f32_sum(x + r * cols, y + r * cols,",
+     "oracle_scan_f32_sum(x, y + r * cols,"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    mutant = oracle.compile_variant(src.replace(old, new), os.path.join(tmp_path, f"{name}.so"))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,10 @@
+"""The CPU oracle checked against what the pages and mathematics fix (no GPU)."""
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(oracle.default())
