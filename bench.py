@@ -1,0 +1,262 @@
+"""Benchmark of libscan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs scan,compact,...]
+
+A step is one device-wide int32 exclusive sum scan of N = 2^28 elements (values
+U{0..15}), inputs resident in HBM.  The headline `value` is Gelem/s over exactly K
+timed steps, bracketed by device synchronisation; HIP events on the stream the
+library launches on give the time.  The JSON line also carries:
+  roofline      achieved algorithmic HBM GB/s of the scan (2 * N * 4 bytes per
+                step) against the 8 TB/s MI355X peak; `traffic` is the measured HBM
+                bytes per launch from rocprofv3 counters (profiles/), or null when
+                the kernel source changed since they were taken;
+  cpu_baseline  the serial CPU oracle timed on this host on the same input;
+  legs          the other workloads: fused compaction (N = 2^27 at 1/50/99 %),
+                float32 sum and int32 max scans (N = 2^26), the two batched row
+                shapes, the 2^20 scan (latency-bound), and a plain device copy of
+                the headline byte count (a practical bandwidth ceiling).
+Only rank 0 of one GPU exists here; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
+SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
+ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+    same kernel source (calibrated against a plain copy), or None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    kv = {}
+    with open(PROFILE_TRAFFIC) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_digest(SCAN_SOURCES):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events recorded on the current (library) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def run(self, fn, steps: int, warmup: int) -> float:
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        self.a.record()
+        for i in range(steps):
+            fn(i)
+        self.b.record()
+        torch.cuda.synchronize()
+        return self.a.elapsed_time(self.b) / steps  # ms per step
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default=",".join(ALL_LEGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+    legs = [s for s in args.legs.split(",") if s]
+    for s in legs:
+        if s not in ALL_LEGS:
+            sys.exit(f"bench.py: unknown leg {s}; choose from {','.join(ALL_LEGS)}")
+
+    import torch
+
+    import prefix_scan_stream_amd as ps
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py: no GPU visible")
+    dev = torch.device("cuda:0")
+    ps.load_library()  # fails loudly if the HIP library is missing
+    timer = Timer(torch)
+    K, W = args.steps, args.warmup
+    result_legs = {}
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    headline = None
+    if "scan" in legs:
+        n = wl.SIZES["big_scan"]
+        log(f"scan: generating int32 U{{0..15}} N={n}")
+        x_host = wl.big_scan()
+        x = to_dev(x_host)
+        out = torch.empty_like(x)
+        log(f"scan: {W} warmup + {K} timed steps")
+        ms = timer.run(lambda i: ps.scan_exclusive(x, "sum", out=out), K, W)
+        # one sampled correctness check of what was timed, against the oracle run below
+        sample_idx = np.random.default_rng(1).integers(0, n, 4096)
+        got_sample = out[torch.from_numpy(sample_idx).to(dev)].cpu().numpy()
+        gelem = n / (ms * 1e-3) / 1e9
+        algo_bytes = 2 * n * 4
+        achieved = algo_bytes / (ms * 1e-3) / 1e9
+        traffic = read_traffic()
+        headline = dict(n=n, ms=ms, gelem=gelem, achieved=achieved, algo_bytes=algo_bytes,
+                        traffic=traffic)
+        log(f"scan: {ms * 1e3:.1f} us/step, {gelem:.1f} Gelem/s, {achieved:.0f} GB/s")
+        cpu = None
+        if not args.no_cpu_baseline:
+            import oracle
+            log("scan: timing the CPU oracle on the same input (serial, 1 thread)")
+            t0 = time.perf_counter()
+            ref = oracle.scan(x_host, "sum", inclusive=False)
+            t1 = time.perf_counter()
+            ok = bool(np.array_equal(ref.y[sample_idx], got_sample))
+            cpu = {"value": round(n / (t1 - t0) / 1e9, 4), "unit": "Gelem/s", "cores": 1,
+                   "kind": "oracle",
+                   "sample": f"the whole workload once: int32 exclusive sum of N={n} "
+                             f"({t1 - t0:.2f} s on 1 of {len(os.sched_getaffinity(0))} host cores)"}
+            headline["sample_check"] = ok
+            if not ok:
+                log("scan: SAMPLED OUTPUT DISAGREES WITH THE ORACLE")
+            del ref
+        headline["cpu"] = cpu
+        del x, out, x_host
+        torch.cuda.empty_cache()
+
+    def rotating(make, sets=3):
+        return [make(i) for i in range(sets)]
+
+    if "small" in legs:
+        x = to_dev(wl.small_scan())
+        out = torch.empty_like(x)
+        ms = timer.run(lambda i: ps.scan_exclusive(x, "sum", out=out), max(K, 50), W)
+        result_legs["small_scan_i32_excl_2e20"] = {"us": round(ms * 1e3, 2),
+                                                   "gelem_s": round(x.numel() / ms / 1e6, 1),
+                                                   "note": "cache-resident, latency-bound"}
+        log(f"small: {ms * 1e3:.2f} us")
+
+    def bw_leg(name, xs, fn, elems, nbytes):
+        outs = [torch.empty_like(t) for t in xs]
+        ms = timer.run(lambda i: fn(xs[i % len(xs)], outs[i % len(outs)]), K, W)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        result_legs[name] = {"us": round(ms * 1e3, 1), "gelem_s": round(elems / ms / 1e6, 1),
+                             "algo_gbs": round(gbs, 1),
+                             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"{name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+
+    if "fp32" in legs:
+        n = wl.SIZES["fp32_scan"]
+        xs = rotating(lambda i: to_dev(wl.fp32_scan()))
+        bw_leg("fp32_sum_incl_2e26", xs, lambda a, b: ps.scan_inclusive(a, "sum", out=b), n, 8 * n)
+        del xs
+    if "max" in legs:
+        n = wl.SIZES["max_scan"]
+        xs = rotating(lambda i: to_dev(wl.max_scan()))
+        bw_leg("i32_max_incl_2e26", xs, lambda a, b: ps.scan_inclusive(a, "max", out=b), n, 8 * n)
+        del xs
+    if "compact" in legs:
+        n = wl.SIZES["compact"]
+        xh = wl.compact_input()
+        xs = rotating(lambda i: to_dev(xh), sets=2)
+        cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        for sel in wl.SELECTIVITIES:
+            thr = wl.threshold_for(sel)
+            kept = int(np.count_nonzero(xh < thr))
+            bw_leg(f"compact_i32_2e27_sel{int(sel * 100)}", xs,
+                   lambda a, b, thr=thr: ps.compact_if(a, "lt", thr, out=b, count=cnt), n,
+                   4 * n + 4 * kept)
+        del xs, xh
+    if "rows64" in legs:
+        xs = rotating(lambda i: to_dev(wl.rows64()))
+        n = xs[0].numel()
+        bw_leg("rows_2e20x64_f32_excl", xs, lambda a, b: ps.batched_row_scan(a, "sum", True, out=b),
+               n, 8 * n)
+        del xs
+    if "rows1024" in legs:
+        xs = rotating(lambda i: to_dev(wl.rows1024()))
+        n = xs[0].numel()
+        bw_leg("rows_2e16x1024_i32_excl", xs,
+               lambda a, b: ps.batched_row_scan(a, "sum", True, out=b), n, 8 * n)
+        del xs
+    if "copy" in legs:
+        n = wl.SIZES["big_scan"]
+        a = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        ms = timer.run(lambda i: b.copy_(a), K, W)
+        gbs = 8 * n / (ms * 1e-3) / 1e9
+        result_legs["device_copy_1GiB"] = {"us": round(ms * 1e3, 1), "gbs": round(gbs, 1),
+                                           "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"copy: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+        del a, b
+
+    if headline is None:
+        print(json.dumps({"legs": result_legs}))
+        return
+    h = headline
+    line = {
+        "metric": "int32 exclusive scan Gelem/s + HBM GB/s (% of peak) at N=2^28; compact Gelem/s",
+        "value": round(h["gelem"], 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(h["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": "int32 exclusive sum scan, N=2^28, values U{0..15} (numpy PCG64)",
+                   "n": h["n"], "scheme": "single-pass decoupled look-back",
+                   "tile_elems": 4096},
+        "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": h["traffic"]},
+        "cpu_baseline": h["cpu"],
+        "sample_check": h.get("sample_check"),
+        "legs": result_legs,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+/*
+ * libscan.h -- device-wide prefix scan and stream compaction for AMD MI355X (gfx950).
+ *
+ * C ABI: plain pointers and sizes, no C++ or framework types.  Unless marked
+ * "host", every pointer is a device pointer (memory from hipMalloc or an
+ * allocator built on it) on the device that is current when the call is made.
+ *
+ * Sources of the operations (page title and section):
+ *   [Scan3]  geek-doc.cn, "并行前缀和 scan: Hillis-Steele、Blelloch 与 warp shuffle
+ *            三种写法": section 一 (inclusive and exclusive scan, the total, and
+ *            compaction by an exclusive scan of predicate flags), 四 (scans larger
+ *            than one block), 五 (warp-level scan), pitfall list.
+ *   [Blog2]  lpnh.cn/news/2866224, parallel scan overview: section 3.3 (a generic
+ *            parallel_scan(in, out, n, op) over any associative operator), 4.1
+ *            (compaction: flags, scan, scatter), 5.3 (work issued on streams),
+ *            7.2 (segmented scans).
+ *   [SIMT3]  pgsm.cn/news/414823, "SIMT数据依赖与并行前缀和：从原理到流压缩实战":
+ *            section 4.2 (compaction writes the kept elements in order and a count
+ *            computed on the device).
+ *
+ * Common rules for every entry point
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t passed
+ *     as void*; NULL = the null stream) and the call returns without waiting.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     non-LS_OK status nothing has been enqueued and no output is written.
+ *   - The caller owns every buffer.  The library allocates and frees nothing
+ *     and never synchronises.
+ *   - Element buffers must be 4-byte aligned.  16-byte alignment of `in` and
+ *     `out` enables 128-bit loads and stores; other alignments are accepted and
+ *     run a slower path.
+ *   - Concurrent calls must use distinct workspaces; calls that share a
+ *     workspace on different streams race.
+ */
+#ifndef LIBSCAN_H
+#define LIBSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LS_ABI_VERSION 1
+
+typedef enum ls_status {
+    LS_OK = 0,
+    LS_ERR_INVALID_ARG = 1, /* bad size, NULL, alignment, enum value, or overlap */
+    LS_ERR_UNSUPPORTED = 2, /* a valid combination the library does not define (float32 xor) */
+    LS_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the size query returned */
+    LS_ERR_HIP = 4          /* the HIP runtime reported an error when enqueuing */
+} ls_status;
+
+/* Element types.  All are 32 bits wide. */
+typedef enum ls_dtype { LS_INT32 = 0, LS_UINT32 = 1, LS_FLOAT32 = 2 } ls_dtype;
+
+/* Associative operators ([Scan3] 一 and 三; [Blog2] 3.3).
+ *   LS_SUM  int32/uint32: addition modulo 2^32 (two's complement wrap);
+ *           float32: IEEE addition; association order is the library's, so
+ *           results may differ from a serial sum in the last bits ([Scan3]
+ *           pitfall list) and may differ between runs.
+ *   LS_MAX  int32 signed, uint32 unsigned, float32 (a > b) ? a : b, which on a
+ *           tie keeps the later element; bit-exact and run-to-run identical for
+ *           data without NaN.  NaN inputs give unspecified results.
+ *   LS_XOR  int32/uint32 bitwise; float32 -> LS_ERR_UNSUPPORTED.
+ * Identity (first exclusive cell, value for n = 0): 0 for sum and xor
+ * (+0.0f for float32), INT32_MIN / 0u / -infinity for max. */
+typedef enum ls_op { LS_SUM = 0, LS_MAX = 1, LS_XOR = 2 } ls_op;
+
+/* Compaction predicates: keep x when (x CMP threshold), compared in the element
+ * type (signed, unsigned, or IEEE float with C semantics: NaN satisfies only NE). */
+typedef enum ls_cmp { LS_LT = 0, LS_LE = 1, LS_GT = 2, LS_GE = 3, LS_EQ = 4, LS_NE = 5 } ls_cmp;
+
+/* Returns LS_ABI_VERSION of the loaded library. */
+int ls_abi_version(void);
+
+/* A static, human-readable string for a status code (never NULL). */
+const char *ls_status_string(ls_status s);
+
+/* Workspace size for scan_inclusive / scan_exclusive.
+ *   bytes (host, out): size of the device workspace a call with these arguments
+ *   needs (never 0).  Errors: LS_ERR_INVALID_ARG for n < 0, bytes == NULL or an
+ *   unknown enum; LS_ERR_UNSUPPORTED for float32 xor. */
+ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t *bytes);
+
+/* Inclusive scan: out[i] = in[0] (+) in[1] (+) ... (+) in[i].     [Scan3] 一
+ * Exclusive scan: out[0] = identity, out[i] = in[0] (+) ... (+) in[i-1].
+ *
+ *   in, out   n elements of type t.  out == in (exact aliasing, in place) is
+ *             allowed; any other overlap is LS_ERR_INVALID_ARG.
+ *   n         element count, 0 <= n.  n == 0 writes only *total (= identity).
+ *   t, op     element type and operator (see ls_op).
+ *   total     nullable; receives one element: the reduction of all n inputs,
+ *             i.e. the value that no exclusive cell holds ([Scan3] 一).
+ *   ws        device workspace of ws_bytes >= ls_scan_workspace_bytes(...),
+ *             4-byte aligned (256-byte aligned is best).  Its contents on entry
+ *             do not matter; the call re-initialises what it uses.
+ *   stream    hipStream_t as void*, or NULL.
+ * One pass over the data: each element is read once and written once. */
+ls_status scan_inclusive(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, void *total,
+                         void *ws, size_t ws_bytes, void *stream);
+ls_status scan_exclusive(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, void *total,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size for compact_if (same rules as ls_scan_workspace_bytes). */
+ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t *bytes);
+
+/* Stable stream compaction ([Scan3] 一; [Blog2] 4.1; [SIMT3] 4.2):
+ * every in[i] with (in[i] CMP threshold) is copied to out, in input order, and
+ * the number kept is written to *count on the device.
+ *
+ *   in             n elements of type t.
+ *   out            capacity n elements; must not overlap `in`.  Cells at index
+ *                  >= *count are not written.
+ *   count          device int64_t, written with the number of kept elements
+ *                  (0 when n == 0).  Must not overlap in/out.
+ *   threshold_bits the 32-bit pattern of the threshold in type t.
+ *   ws, ws_bytes   as for the scans (ls_compact_workspace_bytes).
+ * Uses no atomics on the data path; each element is read once and each kept
+ * element written once. */
+ls_status compact_if(const void *in, void *out, int64_t *count, int64_t n, ls_dtype t, ls_cmp cmp,
+                     uint32_t threshold_bits, void *ws, size_t ws_bytes, void *stream);
+
+/* Row-wise scan of a rows x cols row-major, contiguous matrix: each row is
+ * scanned on its own, with no carry between rows (the uniform-length case of a
+ * segmented scan, [Blog2] 7.2).
+ *
+ *   in, out    rows*cols elements; out == in allowed, other overlap is not.
+ *   rows, cols >= 0; either being 0 is a no-op returning LS_OK.
+ *   exclusive  nonzero: exclusive scan per row, zero: inclusive.
+ * Needs no workspace. */
+ls_status batched_row_scan(const void *in, void *out, int64_t rows, int64_t cols, ls_dtype t,
+                           ls_op op, int exclusive, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSCAN_H */

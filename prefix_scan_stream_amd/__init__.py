@@ -1,0 +1,232 @@
+"""prefix_scan_stream_amd -- Python binding of libscan (MI355X / gfx950).
+
+A thin ctypes layer over the C ABI in include/libscan.h: it checks that tensors
+live on a GPU, passes their pointers, sizes and the current HIP stream, and
+raises LibscanError on a non-OK status.  Every step of the computation runs in
+the library's HIP kernels; there is no other implementation behind these names,
+and importing or calling them fails loudly when libscan.so is missing.
+
+PyTorch supplies device memory and streams only.  Workspaces are cached per
+(device, stream) and grown on demand.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+import torch
+
+__all__ = [
+    "LibscanError", "library_path", "load_library", "ls_abi_version", "ls_status_string",
+    "ls_scan_workspace_bytes", "ls_compact_workspace_bytes", "scan_inclusive", "scan_exclusive",
+    "compact_if", "batched_row_scan", "workspace_for",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libscan.so")
+
+LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = range(5)
+DTYPE_CODES = {"int32": 0, "uint32": 1, "float32": 2}
+OP_CODES = {"sum": 0, "max": 1, "xor": 2}
+CMP_CODES = {"lt": 0, "le": 1, "gt": 2, "ge": 3, "eq": 4, "ne": 5}
+_TORCH_DTYPES = {torch.int32: "int32", torch.float32: "float32"}
+if hasattr(torch, "uint32"):
+    _TORCH_DTYPES[torch.uint32] = "uint32"
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LibscanError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = ls_status_string(status) if _lib is not None else f"status {status}"
+        super().__init__(f"{where}: {msg}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libscan.so (built in-tree by prefix_scan_stream_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"libscan.so not found at {_LIB_PATH}; build it with "
+                "`python -m prefix_scan_stream_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I, U32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                              ctypes.c_size_t)
+        lib.ls_abi_version.argtypes = []
+        lib.ls_abi_version.restype = I
+        lib.ls_status_string.argtypes = [I]
+        lib.ls_status_string.restype = ctypes.c_char_p
+        lib.ls_scan_workspace_bytes.argtypes = [I64, I, I, ctypes.POINTER(SZ)]
+        lib.ls_scan_workspace_bytes.restype = I
+        lib.ls_compact_workspace_bytes.argtypes = [I64, I, ctypes.POINTER(SZ)]
+        lib.ls_compact_workspace_bytes.restype = I
+        for name in ("scan_inclusive", "scan_exclusive"):
+            fn = getattr(lib, name)
+            fn.argtypes = [P, P, I64, I, I, P, P, SZ, P]
+            fn.restype = I
+        lib.compact_if.argtypes = [P, P, P, I64, I, I, U32, P, SZ, P]
+        lib.compact_if.restype = I
+        lib.batched_row_scan.argtypes = [P, P, I64, I64, I, I, I, P]
+        lib.batched_row_scan.restype = I
+        _lib = lib
+        return lib
+
+
+def ls_abi_version() -> int:
+    return load_library().ls_abi_version()
+
+
+def ls_status_string(status: int) -> str:
+    return load_library().ls_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != LS_OK:
+        raise LibscanError(status, where)
+
+
+def ls_scan_workspace_bytes(n: int, dtype: str, op: str) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ls_scan_workspace_bytes(n, DTYPE_CODES[dtype], OP_CODES[op],
+                                                  ctypes.byref(out)), "ls_scan_workspace_bytes")
+    return out.value
+
+
+def ls_compact_workspace_bytes(n: int, dtype: str) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ls_compact_workspace_bytes(n, DTYPE_CODES[dtype], ctypes.byref(out)),
+           "ls_compact_workspace_bytes")
+    return out.value
+
+
+# ------------------------------------------------------------ workspaces
+
+_ws_cache: dict = {}
+
+
+def workspace_for(device: torch.device, stream: torch.cuda.Stream, nbytes: int) -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes for (device, stream)."""
+    key = (device.index, stream.cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        size = max(nbytes, 1 << 16)
+        buf = torch.empty(size, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _dtype_of(x: torch.Tensor) -> str:
+    try:
+        return _TORCH_DTYPES[x.dtype]
+    except KeyError:
+        raise TypeError(f"libscan: unsupported dtype {x.dtype} (int32, uint32, float32)") from None
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libscan: tensors must be on a GPU device")
+
+
+def _stream_handle(device) -> tuple:
+    s = torch.cuda.current_stream(device)
+    return s, ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------ entry points
+
+def _scan(name: str, x: torch.Tensor, op: str, out, total):
+    lib = load_library()
+    _require_gpu(x, out, total)
+    if not x.is_contiguous():
+        raise ValueError("libscan: input must be contiguous")
+    dt = _dtype_of(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
+        raise ValueError("libscan: out must be a contiguous tensor like the input")
+    if total is not None and (total.dtype != x.dtype or total.numel() < 1):
+        raise ValueError("libscan: total must hold one element of the input dtype")
+    n = x.numel()
+    stream, sh = _stream_handle(x.device)
+    need = ls_scan_workspace_bytes(n, dt, op)
+    ws = workspace_for(x.device, stream, need)
+    st = getattr(lib, name)(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], _ptr(total),
+                            _ptr(ws), ws.numel(), sh)
+    _check(st, name)
+    return out
+
+
+def scan_inclusive(x: torch.Tensor, op: str = "sum", out: torch.Tensor | None = None,
+                   total: torch.Tensor | None = None) -> torch.Tensor:
+    """out[i] = x[0] (+) ... (+) x[i] over the flattened tensor; total (optional,
+    one element) receives the reduction of all of x.  out may be x (in place)."""
+    return _scan("scan_inclusive", x, op, out, total)
+
+
+def scan_exclusive(x: torch.Tensor, op: str = "sum", out: torch.Tensor | None = None,
+                   total: torch.Tensor | None = None) -> torch.Tensor:
+    """out[0] = identity, out[i] = x[0] (+) ... (+) x[i-1]."""
+    return _scan("scan_exclusive", x, op, out, total)
+
+
+def compact_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | None = None,
+               count: torch.Tensor | None = None):
+    """Stable compaction of the flattened x under (x CMP threshold).
+
+    Returns (out, count): out has x's size, its first `count` cells hold the kept
+    elements in input order; count is a one-element int64 device tensor."""
+    lib = load_library()
+    _require_gpu(x, out, count)
+    if not x.is_contiguous():
+        raise ValueError("libscan: input must be contiguous")
+    dt = _dtype_of(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=x.device)
+    if count.dtype != torch.int64:
+        raise ValueError("libscan: count must be int64")
+    np_dt = {"int32": "i4", "uint32": "u4", "float32": "f4"}[dt]
+    thr_bits = int(np.array([threshold], dtype=np_dt).view(np.uint32)[0])
+    n = x.numel()
+    stream, sh = _stream_handle(x.device)
+    need = ls_compact_workspace_bytes(n, dt)
+    ws = workspace_for(x.device, stream, need)
+    st = lib.compact_if(_ptr(x), _ptr(out), _ptr(count), n, DTYPE_CODES[dt], CMP_CODES[cmp],
+                        thr_bits, _ptr(ws), ws.numel(), sh)
+    _check(st, "compact_if")
+    return out, count
+
+
+def batched_row_scan(x: torch.Tensor, op: str = "sum", exclusive: bool = True,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Scan each row of a contiguous 2-D tensor independently (no carry between rows)."""
+    lib = load_library()
+    _require_gpu(x, out)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("libscan: batched_row_scan wants a contiguous 2-D tensor")
+    dt = _dtype_of(x)
+    if out is None:
+        out = torch.empty_like(x)
+    rows, cols = x.shape
+    _, sh = _stream_handle(x.device)
+    st = lib.batched_row_scan(_ptr(x), _ptr(out), rows, cols, DTYPE_CODES[dt], OP_CODES[op],
+                              1 if exclusive else 0, sh)
+    _check(st, "batched_row_scan")
+    return out

@@ -1,0 +1,76 @@
+"""Build libscan.so for gfx950 in-tree with hipcc.
+
+    python -m prefix_scan_stream_amd.build          # or build() from Python
+
+Objects go to prefix_scan_stream_amd/_build/ (git-ignored); the shared library
+to prefix_scan_stream_amd/libscan.so.  Only the entry points declared in
+include/libscan.h are exported.
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+HEADER = os.path.join(ROOT, "include", "libscan.h")
+LIB = os.path.join(PKG, "libscan.so")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+          "-I", os.path.join(ROOT, "include")]
+# Packed fp32 VALU forms are kept out of the generated code.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+SOURCES = ["ls_scan.hip", "ls_compact.hip", "ls_batched.hip", "ls_api.cpp"]
+
+
+def exported_symbols() -> list[str]:
+    """Function names declared in include/libscan.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, re.M)
+    return sorted(set(names))
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    path = os.path.join(CSRC, src)
+    if src.endswith(".hip"):
+        cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE, "-c", path, "-o", obj]
+    else:
+        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+    subprocess.check_call(cmd)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    vs = os.path.join(BUILD, "exports.map")
+    with open(vs, "w") as f:
+        f.write("{\n  global:\n")
+        for name in exported_symbols():
+            f.write(f"    {name};\n")
+        f.write("  local: *;\n};\n")
+    tmp = LIB + f".tmp{os.getpid()}"
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+                           f"-Wl,--version-script={vs}"])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

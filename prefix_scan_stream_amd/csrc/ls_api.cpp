@@ -1,0 +1,164 @@
+// ls_api.cpp -- the extern "C" boundary of libscan: validation, sizing, dispatch.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call
+// has no effect and the checks work without a GPU.  See include/libscan.h for
+// the contract of each entry point.
+#include "../../include/libscan.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "ls_internal.hpp"
+
+namespace {
+
+bool valid_dtype(ls_dtype t) { return t == LS_INT32 || t == LS_UINT32 || t == LS_FLOAT32; }
+bool valid_op(ls_op op) { return op == LS_SUM || op == LS_MAX || op == LS_XOR; }
+bool valid_cmp(ls_cmp c) { return c >= LS_LT && c <= LS_NE; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (na == 0 || nb == 0)
+        return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// n elements of 4 bytes must be addressable without wrapping
+bool size_ok(int64_t n) { return n >= 0 && n <= (INT64_MAX / 8); }
+
+ls_status from_hip(hipError_t e) { return e == hipSuccess ? LS_OK : LS_ERR_HIP; }
+
+ls_status check_ws(const void* ws, size_t ws_bytes, size_t need)
+{
+    if (ws == nullptr || ws_bytes < need)
+        return LS_ERR_WORKSPACE;
+    return LS_OK;
+}
+
+ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
+                      void* ws, size_t ws_bytes, void* stream, bool inclusive)
+{
+    if (!size_ok(n) || !valid_dtype(t) || !valid_op(op))
+        return LS_ERR_INVALID_ARG;
+    const size_t bytes = size_t(n) * 4;
+    if (n > 0) {
+        if (in == nullptr || out == nullptr || !aligned(in, 4) || !aligned(out, 4))
+            return LS_ERR_INVALID_ARG;
+        if (in != out && overlaps(in, bytes, out, bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (total != nullptr) {
+        if (!aligned(total, 4) || overlaps(total, 4, in, bytes) || overlaps(total, 4, out, bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (t == LS_FLOAT32 && op == LS_XOR)
+        return LS_ERR_UNSUPPORTED;
+    const size_t need = ls::scan_workspace_bytes(n);
+    ls_status st = check_ws(ws, ws_bytes, need);
+    if (st != LS_OK)
+        return st;
+    if (!aligned(ws, 16) || overlaps(ws, need, in, bytes) || overlaps(ws, need, out, bytes) ||
+        (total != nullptr && overlaps(ws, need, total, 4)))
+        return LS_ERR_INVALID_ARG;
+    return from_hip(ls::launch_scan(in, out, n, int(t), int(op), inclusive, total, ws,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ls_abi_version(void) { return LS_ABI_VERSION; }
+
+const char* ls_status_string(ls_status s)
+{
+    switch (s) {
+    case LS_OK: return "LS_OK: success";
+    case LS_ERR_INVALID_ARG: return "LS_ERR_INVALID_ARG: invalid argument (size, pointer, alignment, enum or overlap)";
+    case LS_ERR_UNSUPPORTED: return "LS_ERR_UNSUPPORTED: operator not defined for this element type";
+    case LS_ERR_WORKSPACE: return "LS_ERR_WORKSPACE: workspace missing or too small";
+    case LS_ERR_HIP: return "LS_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown libscan status";
+}
+
+ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t* bytes)
+{
+    if (bytes == nullptr || !size_ok(n) || !valid_dtype(t) || !valid_op(op))
+        return LS_ERR_INVALID_ARG;
+    if (t == LS_FLOAT32 && op == LS_XOR)
+        return LS_ERR_UNSUPPORTED;
+    *bytes = ls::scan_workspace_bytes(n);
+    return LS_OK;
+}
+
+ls_status scan_inclusive(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
+                         void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, true);
+}
+
+ls_status scan_exclusive(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
+                         void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, false);
+}
+
+ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t* bytes)
+{
+    if (bytes == nullptr || !size_ok(n) || !valid_dtype(t))
+        return LS_ERR_INVALID_ARG;
+    *bytes = ls::compact_workspace_bytes(n);
+    return LS_OK;
+}
+
+ls_status compact_if(const void* in, void* out, int64_t* count, int64_t n, ls_dtype t, ls_cmp cmp,
+                     uint32_t threshold_bits, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!size_ok(n) || !valid_dtype(t) || !valid_cmp(cmp) || count == nullptr || !aligned(count, 8))
+        return LS_ERR_INVALID_ARG;
+    const size_t bytes = size_t(n) * 4;
+    if (n > 0) {
+        if (in == nullptr || out == nullptr || !aligned(in, 4) || !aligned(out, 4))
+            return LS_ERR_INVALID_ARG;
+        if (overlaps(in, bytes, out, bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (overlaps(count, 8, in, bytes) || overlaps(count, 8, out, bytes))
+        return LS_ERR_INVALID_ARG;
+    const size_t need = ls::compact_workspace_bytes(n);
+    ls_status st = check_ws(ws, ws_bytes, need);
+    if (st != LS_OK)
+        return st;
+    if (!aligned(ws, 16) || overlaps(ws, need, in, bytes) || overlaps(ws, need, out, bytes) ||
+        overlaps(ws, need, count, 8))
+        return LS_ERR_INVALID_ARG;
+    return from_hip(ls::launch_compact(in, out, count, n, int(t), int(cmp), threshold_bits, ws,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+ls_status batched_row_scan(const void* in, void* out, int64_t rows, int64_t cols, ls_dtype t,
+                           ls_op op, int exclusive, void* stream)
+{
+    if (rows < 0 || cols < 0 || !valid_dtype(t) || !valid_op(op))
+        return LS_ERR_INVALID_ARG;
+    if (rows > 0 && cols > INT64_MAX / 8 / rows)
+        return LS_ERR_INVALID_ARG;
+    const int64_t n = rows * cols;
+    const size_t bytes = size_t(n) * 4;
+    if (n > 0) {
+        if (in == nullptr || out == nullptr || !aligned(in, 4) || !aligned(out, 4))
+            return LS_ERR_INVALID_ARG;
+        if (in != out && overlaps(in, bytes, out, bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (t == LS_FLOAT32 && op == LS_XOR)
+        return LS_ERR_UNSUPPORTED;
+    return from_hip(ls::launch_batched(in, out, rows, cols, int(t), int(op), exclusive != 0,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

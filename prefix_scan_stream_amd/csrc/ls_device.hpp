@@ -1,0 +1,235 @@
+// ls_device.hpp -- device building blocks of libscan for gfx950 (CDNA4, wave64).
+//
+// Lane level: a 64-lane inclusive scan in six cross-lane steps on DPP (data
+// parallel primitives), no LDS and no barrier.  It is the window-doubling scan of
+// the Hillis-Steele section of the parallel prefix scan page (geek-doc.cn, 二),
+// applied to the lanes of a wavefront as that page's section 五 does for the 32
+// lanes of a warp, with the guard "only lanes at or above the stride add": a lane
+// whose source is out of range receives the operator identity.  Six steps cover
+// 64 lanes where the page's warp needs five for 32.
+//
+// Tile level: each thread holds CHUNKS runs of 4 consecutive elements (one
+// 128-bit word each).  A tile is scanned as: serial scan inside each run, wave
+// scan of the run totals, a scan of the per-(run, wave) totals through LDS, and
+// a carry from earlier tiles -- the "scan inside, scan the totals, add the
+// offset" composition of the page's section 四, arranged so that every global
+// access is a coalesced 128-bit load or store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ls {
+
+// ---------------------------------------------------------------- operators
+// Every combine in the library is written apply(earlier, later).  For the float
+// max that order matters on ties (the later element wins), and keeping it
+// everywhere makes the result independent of how the work is split.
+
+struct SumU32 {
+    using T = uint32_t;
+    static __device__ __forceinline__ T identity() { return 0u; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a + b; }
+};
+struct XorU32 {
+    using T = uint32_t;
+    static __device__ __forceinline__ T identity() { return 0u; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a ^ b; }
+};
+struct MaxU32 {
+    using T = uint32_t;
+    static __device__ __forceinline__ T identity() { return 0u; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a > b ? a : b; }
+};
+struct MaxI32 {
+    using T = int32_t;
+    static __device__ __forceinline__ T identity() { return INT32_MIN; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a > b ? a : b; }
+};
+struct SumF32 {
+    using T = float;
+    static __device__ __forceinline__ T identity() { return 0.0f; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a + b; }
+};
+struct MaxF32 {
+    using T = float;
+    static __device__ __forceinline__ T identity() { return -__builtin_inff(); }
+    static __device__ __forceinline__ T apply(T a, T b) { return a > b ? a : b; }
+};
+
+template <class T>
+__device__ __forceinline__ uint32_t to_bits(T v) { return __builtin_bit_cast(uint32_t, v); }
+template <class T>
+__device__ __forceinline__ T from_bits(uint32_t b) { return __builtin_bit_cast(T, b); }
+
+// ---------------------------------------------------------------- DPP lane moves
+// DPP control words (GFX9 encoding, valid on gfx950).
+enum : int {
+    DPP_ROW_SHR1 = 0x111,
+    DPP_ROW_SHR2 = 0x112,
+    DPP_ROW_SHR4 = 0x114,
+    DPP_ROW_SHR8 = 0x118,
+    DPP_WAVE_SHR1 = 0x138,
+    DPP_ROW_BCAST15 = 0x142,
+    DPP_ROW_BCAST31 = 0x143,
+};
+
+// Lanes whose DPP source is invalid, or whose row is masked off, return `old`.
+template <int CTRL, int ROW_MASK, class T>
+__device__ __forceinline__ T dpp_move(T old, T v)
+{
+    int r = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                        CTRL, ROW_MASK, 0xf, false);
+    return __builtin_bit_cast(T, r);
+}
+
+// Inclusive scan inside each row of 16 lanes (four steps: strides 1, 2, 4, 8).
+template <class Op>
+__device__ __forceinline__ typename Op::T row16_inclusive_scan(typename Op::T v)
+{
+    using T = typename Op::T;
+    const T id = Op::identity();
+    v = Op::apply(dpp_move<DPP_ROW_SHR1, 0xf>(id, v), v);
+    v = Op::apply(dpp_move<DPP_ROW_SHR2, 0xf>(id, v), v);
+    v = Op::apply(dpp_move<DPP_ROW_SHR4, 0xf>(id, v), v);
+    v = Op::apply(dpp_move<DPP_ROW_SHR8, 0xf>(id, v), v);
+    return v;
+}
+
+// Inclusive scan over all 64 lanes: the row scan, then lane 15 of rows 0 and 2
+// is added into rows 1 and 3, then lane 31 into rows 2 and 3.
+template <class Op>
+__device__ __forceinline__ typename Op::T wave_inclusive_scan(typename Op::T v)
+{
+    using T = typename Op::T;
+    const T id = Op::identity();
+    v = row16_inclusive_scan<Op>(v);
+    v = Op::apply(dpp_move<DPP_ROW_BCAST15, 0xa>(id, v), v);
+    v = Op::apply(dpp_move<DPP_ROW_BCAST31, 0xc>(id, v), v);
+    return v;
+}
+
+// Exclusive value from an inclusive one: shift up one lane, lane 0 gets identity.
+template <class Op>
+__device__ __forceinline__ typename Op::T wave_shift_up(typename Op::T incl)
+{
+    return dpp_move<DPP_WAVE_SHR1, 0xf>(Op::identity(), incl);
+}
+
+// The same inside rows of 16: lane 0 of each row gets identity.
+template <class Op>
+__device__ __forceinline__ typename Op::T row16_shift_up(typename Op::T incl)
+{
+    return dpp_move<DPP_ROW_SHR1, 0xf>(Op::identity(), incl);
+}
+
+template <class T>
+__device__ __forceinline__ T read_lane(T v, int lane)
+{
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- 128-bit tile I/O
+// A run of 4 consecutive 32-bit elements.  `full` runs use one 128-bit access;
+// partial runs (the ragged tail) use element accesses, padding with `fill`.
+template <class T>
+struct Run4 {
+    T v[4];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T, bool VEC>
+__device__ __forceinline__ Run4<T> load_run(const T* __restrict__ p, int64_t idx, int64_t n, T fill)
+{
+    Run4<T> r;
+    if (idx + 4 <= n) {
+        if constexpr (VEC) {
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + idx));
+            r.v[0] = from_bits<T>(w.x);
+            r.v[1] = from_bits<T>(w.y);
+            r.v[2] = from_bits<T>(w.z);
+            r.v[3] = from_bits<T>(w.w);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                r.v[k] = p[idx + k];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            r.v[k] = (idx + k < n) ? p[idx + k] : fill;
+    }
+    return r;
+}
+
+template <class T, bool VEC>
+__device__ __forceinline__ void store_run(T* __restrict__ p, int64_t idx, int64_t n, const Run4<T>& r)
+{
+    if (idx + 4 <= n) {
+        if constexpr (VEC) {
+            u32x4 w;
+            w.x = to_bits(r.v[0]);
+            w.y = to_bits(r.v[1]);
+            w.z = to_bits(r.v[2]);
+            w.w = to_bits(r.v[3]);
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p + idx));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                p[idx + k] = r.v[k];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (idx + k < n)
+                p[idx + k] = r.v[k];
+    }
+}
+
+// ---------------------------------------------------------------- tile status words
+// One 64-bit word per tile, published and read with agent-scope atomics, so the
+// flag and the value travel together and no other memory needs ordering.  Agent
+// scope makes the accesses coherent across the eight XCDs (their L2s are not).
+//   32-bit payload (scans): bits 63..32 = flag, bits 31..0 = value bits.
+//   62-bit payload (compaction counts): bits 63..62 = flag, bits 61..0 = count.
+enum : uint32_t { ST_EMPTY = 0, ST_AGGREGATE = 1, ST_PREFIX = 2 };
+
+__device__ __forceinline__ void status_store(uint64_t* p, uint64_t w)
+{
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t status_load(const uint64_t* p)
+{
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded waiting: a look-back gives up after this many empty polls and records
+// the fact in the workspace error word, so a defect can never hang the GPU.  In
+// a correct run the wait is a few microseconds; the cap is far above that.
+constexpr int LOOKBACK_SPIN_LIMIT = 1 << 16;
+constexpr uint32_t WS_ERR_LOOKBACK_TIMEOUT = 1u;
+
+// Workspace header (first 256 bytes of every workspace).
+struct WsHeader {
+    uint32_t tile_counter;  // dynamic tile ids: the order in which blocks start
+    uint32_t error_flags;   // WS_ERR_* bits of the last call
+    uint32_t pad[62];
+};
+static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
+
+// Tile id in start order: a block only ever waits for tiles that were handed to
+// blocks which started before it, so every wait is for a running block.
+__device__ __forceinline__ uint32_t take_tile_id(WsHeader* h)
+{
+    return __hip_atomic_fetch_add(&h->tile_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits)
+{
+    __hip_atomic_fetch_or(&h->error_flags, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace ls

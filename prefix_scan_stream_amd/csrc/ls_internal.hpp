@@ -1,0 +1,33 @@
+// ls_internal.hpp -- launchers shared between the kernel files and the C ABI layer.
+// Host-side C++ only; the public interface is include/libscan.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ls {
+
+// Element-type and operator codes (the values of ls_dtype / ls_op / ls_cmp).
+enum Dtype : int { DT_INT32 = 0, DT_UINT32 = 1, DT_FLOAT32 = 2 };
+enum OpCode : int { OP_SUM = 0, OP_MAX = 1, OP_XOR = 2 };
+
+// ---- single-pass device-wide scan (ls_scan.hip)
+// Zeroes the workspace header and `status_words` tile status words after it.
+hipError_t clear_workspace(void* ws, int64_t status_words, hipStream_t stream);
+int64_t scan_tile_elems();
+size_t scan_workspace_bytes(int64_t n);
+hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, bool inclusive,
+                       void* total, void* ws, hipStream_t stream);
+
+// ---- fused compaction (ls_compact.hip)
+int64_t compact_tile_elems();
+size_t compact_workspace_bytes(int64_t n);
+hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, int dtype, int cmp,
+                          uint32_t threshold_bits, void* ws, hipStream_t stream);
+
+// ---- batched row scan (ls_batched.hip)
+hipError_t launch_batched(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int op,
+                          bool exclusive, hipStream_t stream);
+
+}  // namespace ls

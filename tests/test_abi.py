@@ -1,0 +1,149 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/libscan.h declares, and rejects bad arguments on the host before any
+HIP call (each call here is built to fail validation; none enqueues work)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import prefix_scan_stream_amd as ps
+from prefix_scan_stream_amd import build as psb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libscan.h")
+
+INV, UNS, WS = ps.LS_ERR_INVALID_ARG, ps.LS_ERR_UNSUPPORTED, ps.LS_ERR_WORKSPACE
+INT32, UINT32, F32 = 0, 1, 2
+SUM, MAX, XOR = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ps.library_path()):
+        psb.build()
+    return ps.load_library()
+
+
+def declared_functions():
+    return psb.exported_symbols()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("scan_inclusive", "scan_exclusive", "compact_if", "batched_row_scan",
+                 "ls_scan_workspace_bytes", "ls_compact_workspace_bytes", "ls_status_string",
+                 "ls_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ps.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing else leaks out of the library
+    assert exported == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert ps.ls_abi_version() == 1
+    for s in range(5):
+        assert ps.ls_status_string(s).startswith("LS_")
+    assert "unknown" in ps.ls_status_string(99)
+
+
+def test_workspace_queries(lib):
+    b0 = ps.ls_scan_workspace_bytes(0, "int32", "sum")
+    b1 = ps.ls_scan_workspace_bytes(1 << 28, "int32", "sum")
+    assert b0 > 0 and b0 % 256 == 0
+    assert b1 >= 256 + 8 * ((1 << 28) // 4096)
+    assert ps.ls_compact_workspace_bytes(1 << 27, "int32") >= 256 + 8 * ((1 << 27) // 4096)
+    sz = ctypes.c_size_t(0)
+    assert lib.ls_scan_workspace_bytes(-1, INT32, SUM, ctypes.byref(sz)) == INV
+    assert lib.ls_scan_workspace_bytes(10, 7, SUM, ctypes.byref(sz)) == INV
+    assert lib.ls_scan_workspace_bytes(10, INT32, 9, ctypes.byref(sz)) == INV
+    assert lib.ls_scan_workspace_bytes(10, F32, XOR, ctypes.byref(sz)) == UNS
+    assert lib.ls_scan_workspace_bytes(10, INT32, SUM, None) == INV
+    assert lib.ls_compact_workspace_bytes(-5, INT32, ctypes.byref(sz)) == INV
+
+
+# Fake, never-dereferenced addresses: every call below must be rejected on the host.
+A_IN = 0x7F0000000000
+A_OUT = 0x7F0010000000
+A_WS = 0x7F0020000000
+A_TOT = 0x7F0030000000
+BIG_WS = 1 << 30
+
+
+def _scan(lib, fn, inp, out, n, t=INT32, op=SUM, total=None, ws=A_WS, wsb=BIG_WS):
+    f = getattr(lib, fn)
+    return f(inp, out, n, t, op, total, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["scan_inclusive", "scan_exclusive"])
+def test_scan_validation(lib, fn):
+    assert _scan(lib, fn, A_IN, A_OUT, -1) == INV                      # negative n
+    assert _scan(lib, fn, None, A_OUT, 10) == INV                      # NULL input
+    assert _scan(lib, fn, A_IN, None, 10) == INV                       # NULL output
+    assert _scan(lib, fn, A_IN + 2, A_OUT, 10) == INV                  # misaligned
+    assert _scan(lib, fn, A_IN, A_OUT + 1, 10) == INV
+    assert _scan(lib, fn, A_IN, A_IN + 4, 10) == INV                   # partial overlap
+    assert _scan(lib, fn, A_IN, A_OUT, 10, t=3) == INV                 # bad dtype
+    assert _scan(lib, fn, A_IN, A_OUT, 10, op=5) == INV                # bad op
+    assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=XOR) == UNS       # float xor
+    assert _scan(lib, fn, A_IN, A_OUT, 10, ws=None) == WS              # no workspace
+    assert _scan(lib, fn, A_IN, A_OUT, 1 << 20, wsb=64) == WS          # workspace too small
+    assert _scan(lib, fn, A_IN, A_OUT, 10, ws=A_WS + 8) == INV         # workspace misaligned
+    assert _scan(lib, fn, A_IN, A_OUT, 1000, ws=A_OUT + 16) == INV     # workspace overlaps out
+    assert _scan(lib, fn, A_IN, A_OUT, 10, total=A_OUT + 8) == INV     # total inside out
+    assert _scan(lib, fn, A_IN, A_OUT, 10, total=A_TOT + 2) == INV     # total misaligned
+    # error precedence: invalid argument before unsupported before workspace
+    assert _scan(lib, fn, None, A_OUT, 10, t=F32, op=XOR, ws=None) == INV
+    assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=XOR, ws=None) == UNS
+
+
+def test_compact_validation(lib):
+    def call(inp=A_IN, out=A_OUT, count=A_TOT, n=10, t=INT32, cmp=0, ws=A_WS, wsb=BIG_WS):
+        return lib.compact_if(inp, out, count, n, t, cmp, 5, ws, wsb, None)
+
+    assert call(n=-1) == INV
+    assert call(count=None) == INV
+    assert call(count=A_TOT + 4) == INV         # count must be 8-byte aligned
+    assert call(inp=None) == INV
+    assert call(out=A_IN) == INV                # compaction never runs in place
+    assert call(out=A_IN + 16) == INV
+    assert call(cmp=6) == INV
+    assert call(t=9) == INV
+    assert call(count=A_OUT + 8) == INV         # count inside out
+    assert call(ws=None) == WS
+    assert call(n=1 << 20, wsb=256) == WS
+
+
+def test_batched_validation(lib):
+    def call(inp=A_IN, out=A_OUT, rows=4, cols=64, t=F32, op=SUM, excl=1):
+        return lib.batched_row_scan(inp, out, rows, cols, t, op, excl, None)
+
+    assert call(rows=-1) == INV
+    assert call(cols=-1) == INV
+    assert call(inp=None) == INV
+    assert call(out=A_IN + 4) == INV
+    assert call(t=F32, op=XOR) == UNS
+    assert call(rows=1 << 40, cols=1 << 40) == INV  # size overflow
+    # empty shapes are a no-op even with NULL pointers (nothing is enqueued)
+    assert call(inp=None, out=None, rows=0) == ps.LS_OK
+    assert call(inp=None, out=None, cols=0) == ps.LS_OK
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        ps.scan_exclusive(x)
+    with pytest.raises(ValueError):
+        ps.compact_if(x, "lt", 3)
+    with pytest.raises(ValueError):
+        ps.batched_row_scan(x.reshape(2, 4))
