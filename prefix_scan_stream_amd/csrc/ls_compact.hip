@@ -23,15 +23,11 @@ namespace ls {
 
 constexpr int CP_BLOCK = 256;
 constexpr int CP_WAVES = CP_BLOCK / 64;
-constexpr int CP_CHUNKS = 4;
-constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;  // 4096 elements, 16 KiB staged in LDS
-
-// Count status words: flag in bits 63..62, count in bits 61..0.
-constexpr uint64_t CNT_MASK = (uint64_t(1) << 62) - 1;
-__device__ __forceinline__ uint64_t pack_count(uint32_t flag, uint64_t c)
-{
-    return (uint64_t(flag) << 62) | (c & CNT_MASK);
-}
+#ifndef LS_CP_CHUNKS
+#define LS_CP_CHUNKS 16
+#endif
+constexpr int CP_CHUNKS = LS_CP_CHUNKS;
+constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;  // 16384 elements (64 KiB staged in LDS) by default
 
 // Predicate through a 4-entry truth table indexed by the comparison outcome:
 // 0 = greater, 1 = less, 2 = equal, 3 = unordered (a NaN is involved).
@@ -51,46 +47,6 @@ __device__ __forceinline__ uint32_t pred_bit(uint32_t v, uint32_t t, uint32_t ta
     return (table >> state) & 1u;
 }
 
-// Number of elements kept by all tiles before `tile` (>= 1).  Same walk as the
-// scan's look-back: lanes above the highest lane holding a full prefix carry
-// per-tile counts (each <= CP_TILE, so their sum fits 32 bits); the full prefix
-// itself is a 62-bit count read from that lane.
-__device__ int64_t lookback_count(const uint64_t* status, int64_t tile, WsHeader* hdr)
-{
-    const int lane = lane_id();
-    int64_t excl = 0;
-    int64_t last = tile - 1;
-    int spins = 0;
-    for (;;) {
-        const int64_t idx = last - 63 + lane;
-        const uint64_t w = (idx >= 0) ? status_load(status + idx) : pack_count(ST_PREFIX, 0);
-        const uint32_t flag = uint32_t(w >> 62);
-        const uint64_t empty = __ballot(flag == ST_EMPTY);
-        const uint64_t full = __ballot(flag == ST_PREFIX);
-        const int hi = full ? 63 - __builtin_clzll(full) : -1;
-        const uint64_t needed = (hi >= 0) ? (~0ull << hi) : ~0ull;
-        if (empty & needed) {
-            if (++spins < LOOKBACK_SPIN_LIMIT) {
-                __builtin_amdgcn_s_sleep(1);
-                continue;
-            }
-            if (lane == 0)
-                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
-            return excl;
-        }
-        const uint32_t part = (lane > hi) ? uint32_t(w & CNT_MASK) : 0u;
-        const uint32_t sum = read_lane(wave_inclusive_scan<SumU32>(part), 63);
-        excl += int64_t(sum);
-        if (hi >= 0) {
-            const uint32_t lo32 = __builtin_amdgcn_readlane(uint32_t(w), hi);
-            const uint32_t hi32 = __builtin_amdgcn_readlane(uint32_t(w >> 32), hi);
-            excl += int64_t(((uint64_t(hi32) << 32) | lo32) & CNT_MASK);
-            return excl;
-        }
-        last -= 64;
-    }
-}
-
 template <int DT, bool VEC>
 __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __restrict__ in,
                                                            uint32_t* __restrict__ out, int64_t n,
@@ -98,9 +54,13 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
                                                            uint32_t table, WsHeader* hdr,
                                                            uint64_t* status, int64_t* count)
 {
+    constexpr int PARTS = CP_CHUNKS * CP_WAVES;  // (run, wave) kept counts per tile
+    constexpr uint32_t RUN_STRIDE = CP_BLOCK * 16u;
+    static_assert(PARTS <= 64, "the (run, wave) counts are scanned by one wave");
     __shared__ uint32_t s_items[CP_TILE];
-    __shared__ uint32_t s_tot[CP_CHUNKS][CP_WAVES];
+    __shared__ uint32_t s_part[PARTS];
     __shared__ uint32_t s_tile;
+    __shared__ uint32_t s_kept;
     __shared__ int64_t s_base;
 
     const int tid = threadIdx.x;
@@ -112,20 +72,28 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
     __syncthreads();
     const int64_t tile = s_tile;
     const int64_t tbase = tile * CP_TILE;
+    const int64_t rem = n - tbase;
+    const uint32_t valid = rem < CP_TILE ? uint32_t(rem) : uint32_t(CP_TILE);
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
+    const uint32_t voff = uint32_t(tid) * 16u;
 
+    // 1. load; predicate in registers (elements past n are never kept)
     Run4<uint32_t> r[CP_CHUNKS];
     uint32_t keep[CP_CHUNKS];  // bit k: element k of the run is kept
 #pragma unroll
+    for (int j = 0; j < CP_CHUNKS; ++j)
+        r[j] = load_run_x1<uint32_t>(rin, voff, j * RUN_STRIDE);
+#pragma unroll
     for (int j = 0; j < CP_CHUNKS; ++j) {
-        const int64_t idx = tbase + 4 * int64_t(j * CP_BLOCK + tid);
-        r[j] = load_run<uint32_t, VEC>(in, idx, n, 0u);
+        const uint32_t e0 = 4u * uint32_t(j * CP_BLOCK + tid);
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            m |= (idx + k < n ? pred_bit<DT>(r[j].v[k], thr, table) : 0u) << k;
+            m |= (e0 + k < valid ? pred_bit<DT>(r[j].v[k], thr, table) : 0u) << k;
         keep[j] = m;
     }
 
+    // 2. counts per run, wave scan of the counts, (run, wave) counts to LDS
     uint32_t wex[CP_CHUNKS];
 #pragma unroll
     for (int j = 0; j < CP_CHUNKS; ++j) {
@@ -133,26 +101,30 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
         const uint32_t inc = wave_inclusive_scan<SumU32>(c);
         wex[j] = inc - c;
         if (lane == 63)
-            s_tot[j][wave] = inc;
+            s_part[j * CP_WAVES + wave] = inc;
     }
     __syncthreads();
 
-    uint32_t pre[CP_CHUNKS];
-    uint32_t agg = 0;
-#pragma unroll
-    for (int jj = 0; jj < CP_CHUNKS; ++jj) {
-#pragma unroll
-        for (int ww = 0; ww < CP_WAVES; ++ww) {
-            if (ww == wave)
-                pre[jj] = agg;
-            agg += s_tot[jj][ww];
+    // 3. wave 0: tile-local exclusive offsets of the (run, wave) parts; publish
+    // the tile's count so later tiles can use it before this tile is done
+    if (wave == 0) {
+        const uint32_t v = lane < PARTS ? s_part[lane] : 0u;
+        const uint32_t inc = wave_inclusive_scan<SumU32>(v);
+        const uint32_t kept = read_lane(inc, 63);
+        if (lane < PARTS)
+            s_part[lane] = inc - v;
+        if (lane == 0) {
+            s_kept = kept;
+            status_store(status + tile, CountCodec::pack(tile == 0 ? ST_PREFIX : ST_AGGREGATE, kept));
         }
     }
+    __syncthreads();
+    const uint32_t kept = s_kept;
 
-    // stage kept elements at their rank within the tile
+    // 4. stage kept elements in LDS at their rank inside the tile (input order)
 #pragma unroll
     for (int j = 0; j < CP_CHUNKS; ++j) {
-        uint32_t rank = pre[j] + wex[j];
+        uint32_t rank = s_part[j * CP_WAVES + wave] + wex[j];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (keep[j] & (1u << k))
@@ -160,17 +132,13 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
         }
     }
 
+    // 5. wave 0: number of elements kept by all earlier tiles (the output offset)
     if (wave == 0) {
         int64_t base = 0;
-        if (tile == 0) {
+        if (tile != 0) {
+            base = int64_t(lookback<CountCodec>(status, tile, hdr));
             if (lane == 0)
-                status_store(status, pack_count(ST_PREFIX, agg));
-        } else {
-            if (lane == 0)
-                status_store(status + tile, pack_count(ST_AGGREGATE, agg));
-            base = lookback_count(status, tile, hdr);
-            if (lane == 0)
-                status_store(status + tile, pack_count(ST_PREFIX, uint64_t(base) + agg));
+                status_store(status + tile, CountCodec::pack(ST_PREFIX, uint64_t(base) + kept));
         }
         if (lane == 0)
             s_base = base;
@@ -178,11 +146,34 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
     __syncthreads();
     const int64_t base = s_base;
 
-    uint32_t* dst = out + base;
-    for (uint32_t i = tid; i < agg; i += CP_BLOCK)
-        dst[i] = s_items[i];
+    // 6. contiguous copy LDS -> out[base ...]: 32-bit stores up to the first
+    // 16-byte boundary of the output, then 128-bit stores, then a 32-bit tail
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + base, kept * 4u);
+    if (VEC) {
+        const uint32_t mis = uint32_t(reinterpret_cast<uintptr_t>(out + base) >> 2) & 3u;
+        uint32_t head = (4u - mis) & 3u;
+        head = head < kept ? head : kept;
+        if (uint32_t(tid) < head)
+            __builtin_amdgcn_raw_buffer_store_b32(s_items[tid], rout, uint32_t(tid) * 4u, 0, STORE_POLICY);
+        const uint32_t groups = (kept - head) >> 2;
+        for (uint32_t g = tid; g < groups; g += CP_BLOCK) {
+            const uint32_t i = head + 4u * g;
+            u32x4 w;
+            w.x = s_items[i];
+            w.y = s_items[i + 1];
+            w.z = s_items[i + 2];
+            w.w = s_items[i + 3];
+            __builtin_amdgcn_raw_buffer_store_b128(w, rout, i * 4u, 0, STORE_POLICY);
+        }
+        const uint32_t i = head + 4u * groups + uint32_t(tid);
+        if (i < kept)
+            __builtin_amdgcn_raw_buffer_store_b32(s_items[i], rout, i * 4u, 0, STORE_POLICY);
+    } else {
+        for (uint32_t i = tid; i < kept; i += CP_BLOCK)
+            __builtin_amdgcn_raw_buffer_store_b32(s_items[i], rout, i * 4u, 0, STORE_POLICY);
+    }
     if (tile == num_tiles - 1 && tid == 0)
-        *count = base + int64_t(agg);
+        *count = base + int64_t(kept);
 }
 
 __global__ void store_i64_kernel(int64_t* p, int64_t v)
@@ -233,7 +224,7 @@ hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, 
         return e;
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
-    const bool vec = (reinterpret_cast<uintptr_t>(in) & 15) == 0;
+    const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
     const auto* pin = reinterpret_cast<const uint32_t*>(in);
     auto* pout = reinterpret_cast<uint32_t*>(out);
     const uint32_t table = truth_table(cmp);

@@ -131,9 +131,8 @@ __device__ __forceinline__ T read_lane(T v, int lane)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// ---------------------------------------------------------------- 128-bit tile I/O
-// A run of 4 consecutive 32-bit elements.  `full` runs use one 128-bit access;
-// partial runs (the ragged tail) use element accesses, padding with `fill`.
+// ---------------------------------------------------------------- tile I/O
+// A run of 4 consecutive 32-bit elements.
 template <class T>
 struct Run4 {
     T v[4];
@@ -141,6 +140,70 @@ struct Run4 {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resources: a per-tile (base, byte count) window in scalar registers.
+// Loads past the byte count return 0 and stores past it are dropped by the
+// hardware, so a ragged tail needs no per-element branches; offsets are a lane
+// offset in a VGPR plus a per-run constant in an SGPR.  Word 3 selects raw
+// 32-bit dword access for the GFX9-family descriptor layout.
+constexpr int BUF_DWORD3 = 0x00020000;
+constexpr int CACHE_NT = 2;  // streaming (non-temporal) policy for data read or written once
+#ifndef LS_STORE_POLICY
+#define LS_STORE_POLICY 2
+#endif
+constexpr int STORE_POLICY = LS_STORE_POLICY;  // cache policy of the output stores
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), BUF_DWORD3);
+}
+
+// One 128-bit access (base and offsets 16-byte aligned, run fully in range).
+template <class T>
+__device__ __forceinline__ Run4<T> load_run_x4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff)
+{
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, CACHE_NT);
+    Run4<T> r;
+    r.v[0] = from_bits<T>(w.x);
+    r.v[1] = from_bits<T>(w.y);
+    r.v[2] = from_bits<T>(w.z);
+    r.v[3] = from_bits<T>(w.w);
+    return r;
+}
+
+// Four 32-bit accesses: any 4-byte alignment; each element range-checked alone,
+// elements past the window read as 0.
+template <class T>
+__device__ __forceinline__ Run4<T> load_run_x1(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff)
+{
+    Run4<T> r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        r.v[k] = from_bits<T>(__builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4 * k, soff, CACHE_NT));
+    return r;
+}
+
+template <class T>
+__device__ __forceinline__ void store_run_x4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                             const Run4<T>& r)
+{
+    u32x4 w;
+    w.x = to_bits(r.v[0]);
+    w.y = to_bits(r.v[1]);
+    w.z = to_bits(r.v[2]);
+    w.w = to_bits(r.v[3]);
+    __builtin_amdgcn_raw_buffer_store_b128(w, rs, voff, soff, STORE_POLICY);
+}
+
+template <class T>
+__device__ __forceinline__ void store_run_x1(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                             const Run4<T>& r)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        __builtin_amdgcn_raw_buffer_store_b32(to_bits(r.v[k]), rs, voff + 4 * k, soff, STORE_POLICY);
+}
+
+// Element-wise global access with an explicit range check (row kernels).
 template <class T, bool VEC>
 __device__ __forceinline__ Run4<T> load_run(const T* __restrict__ p, int64_t idx, int64_t n, T fill)
 {
@@ -230,6 +293,117 @@ __device__ __forceinline__ uint32_t take_tile_id(WsHeader* h)
 __device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits)
 {
     __hip_atomic_fetch_or(&h->error_flags, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- look-back
+// Status codecs: how a 64-bit status word holds (flag, value) and how values of
+// a window are combined across a wave.
+//
+// Scan values: the operator's 32-bit element, flag in the high half.
+template <class Op>
+struct ScanCodec {
+    using V = typename Op::T;
+    static __device__ __forceinline__ uint32_t flag(uint64_t w) { return uint32_t(w >> 32); }
+    static __device__ __forceinline__ V value(uint64_t w) { return from_bits<V>(uint32_t(w)); }
+    static __device__ __forceinline__ uint64_t pack(uint32_t f, V v)
+    {
+        return (uint64_t(f) << 32) | uint64_t(to_bits(v));
+    }
+    static __device__ __forceinline__ V identity() { return Op::identity(); }
+    static __device__ __forceinline__ V apply(V a, V b) { return Op::apply(a, b); }
+    // Combine the lanes' partials in lane order (lanes below `hi` hold identity).
+    static __device__ __forceinline__ V wave_reduce(V part, int /*hi*/)
+    {
+        return read_lane(wave_inclusive_scan<Op>(part), 63);
+    }
+};
+
+// Compaction counts: 62-bit count, flag in the top two bits.  A lane's partial
+// is small (a few tile counts) except on lane `hi`, whose partial includes a
+// full prefix; the small ones are summed in 32 bits, the big one read whole.
+struct CountCodec {
+    using V = uint64_t;
+    static constexpr uint64_t MASK = (uint64_t(1) << 62) - 1;
+    static __device__ __forceinline__ uint32_t flag(uint64_t w) { return uint32_t(w >> 62); }
+    static __device__ __forceinline__ V value(uint64_t w) { return w & MASK; }
+    static __device__ __forceinline__ uint64_t pack(uint32_t f, V v) { return (uint64_t(f) << 62) | (v & MASK); }
+    static __device__ __forceinline__ V identity() { return 0; }
+    static __device__ __forceinline__ V apply(V a, V b) { return a + b; }
+    static __device__ __forceinline__ V wave_reduce(V part, int hi)
+    {
+        const uint32_t small = (lane_id() > hi) ? uint32_t(part) : 0u;
+        V r = read_lane(wave_inclusive_scan<SumU32>(small), 63);
+        if (hi >= 0) {
+            const uint32_t lo32 = __builtin_amdgcn_readlane(uint32_t(part), hi);
+            const uint32_t hi32 = __builtin_amdgcn_readlane(uint32_t(part >> 32), hi);
+            r += (uint64_t(hi32) << 32) | lo32;
+        }
+        return r;
+    }
+};
+
+// Exclusive prefix of tile `tile` (>= 1), computed by one full wave from the
+// tile status words.  Each poll reads a window of LB_WINDOW tiles (256 by
+// default), lane l holding tiles base + 4l .. base + 4l + 3, so one memory round trip covers four
+// times what one word per lane would; the window size bounds how fast the chain
+// of full prefixes can advance (tiles per round trip).  In the window, the
+// newest tile that has published a full prefix ends the walk: the answer is the
+// operator over it and every newer tile of the window.  Without one, all 256
+// totals are combined and the window moves 256 tiles back.  An empty word newer
+// than the stopping tile means that tile has not published yet: poll again.
+#ifndef LS_LB_PER_LANE
+#define LS_LB_PER_LANE 1
+#endif
+constexpr int LB_PER_LANE = LS_LB_PER_LANE;
+constexpr int LB_WINDOW = 64 * LB_PER_LANE;
+
+template <class Codec>
+__device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHeader* hdr)
+{
+    using V = typename Codec::V;
+    const int lane = lane_id();
+    V excl = Codec::identity();
+    int64_t last = tile - 1;
+    int spins = 0;
+    for (;;) {
+        const int64_t base = last - (LB_WINDOW - 1) + LB_PER_LANE * lane;
+        uint64_t w[LB_PER_LANE];
+#pragma unroll
+        for (int q = 0; q < LB_PER_LANE; ++q) {
+            const int64_t idx = base + q;
+            w[q] = (idx >= 0) ? status_load(status + idx) : Codec::pack(ST_PREFIX, Codec::identity());
+        }
+        int lq = -1;  // newest tile of this lane with a full prefix
+#pragma unroll
+        for (int q = 0; q < LB_PER_LANE; ++q)
+            if (Codec::flag(w[q]) == ST_PREFIX)
+                lq = q;
+        const uint64_t has = __ballot(lq >= 0);
+        const int hi = has ? 63 - __builtin_clzll(has) : -1;
+        const int stop = hi >= 0 ? LB_PER_LANE * hi + __builtin_amdgcn_readlane(lq, hi) : -1;
+        bool waiting = false;
+#pragma unroll
+        for (int q = 0; q < LB_PER_LANE; ++q)
+            waiting |= (LB_PER_LANE * lane + q > stop) && Codec::flag(w[q]) == ST_EMPTY;
+        if (__ballot(waiting)) {
+            if (++spins < LOOKBACK_SPIN_LIMIT) {
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            if (lane == 0)
+                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
+            return excl;  // only reached on a defect; the error word reports it
+        }
+        V part = Codec::identity();
+#pragma unroll
+        for (int q = 0; q < LB_PER_LANE; ++q)
+            if (LB_PER_LANE * lane + q >= stop)
+                part = Codec::apply(part, Codec::value(w[q]));
+        excl = Codec::apply(Codec::wave_reduce(part, hi), excl);  // older tiles on the left
+        if (hi >= 0)
+            return excl;
+        last -= LB_WINDOW;
+    }
 }
 
 }  // namespace ls

@@ -11,9 +11,9 @@
 //      blocks already running) and loads its tile with 128-bit loads;
 //   2. it scans the tile in registers (serial runs of 4, DPP wave scan, LDS scan
 //      of the per-wave totals) and publishes the tile total;
-//   3. its first wave looks back over the 64 preceding tiles at a time, summing
-//      published totals until it meets a tile that has published its full
-//      prefix, then publishes its own full prefix;
+//   3. its first wave looks back over the preceding tiles, 256 per poll,
+//      combining published totals until it meets a tile that has published its
+//      full prefix, then publishes its own full prefix;
 //   4. it writes prefix (+) local scan with 128-bit stores.
 // Each tile status is one 64-bit word (flag + value) so a single atomic access
 // carries both; see ls_device.hpp.
@@ -22,68 +22,56 @@
 
 namespace ls {
 
-constexpr int SCAN_BLOCK = 256;                       // 4 waves
+#ifndef LS_SCAN_BLOCK
+#define LS_SCAN_BLOCK 256
+#endif
+constexpr int SCAN_BLOCK = LS_SCAN_BLOCK;             // 4 waves by default
 constexpr int SCAN_WAVES = SCAN_BLOCK / 64;
-constexpr int SCAN_CHUNKS = 4;                        // 128-bit runs per thread
-constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_CHUNKS * 4;  // 4096 elements
+#ifndef LS_SCAN_CHUNKS
+#define LS_SCAN_CHUNKS 16
+#endif
+constexpr int SCAN_CHUNKS = LS_SCAN_CHUNKS;           // 128-bit runs per thread
+constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_CHUNKS * 4;  // 16384 elements by default
 
-static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "run totals must fit one wave");
+static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanned by one wave");
 
-template <class T>
-__device__ __forceinline__ uint64_t pack32(uint32_t flag, T v)
-{
-    return (uint64_t(flag) << 32) | uint64_t(to_bits(v));
-}
-
-// Exclusive prefix of tile `tile` (>= 1) from the tile status words.  Runs on one
-// full wave.  Window: lanes 0..63 look at tiles last-63 .. last.  If some lane sees
-// a full prefix, the highest such lane ends the walk: the answer is the operator
-// over that lane and all lanes above it.  Otherwise all 64 totals are combined and
-// the window moves 64 tiles back.  Any empty word at or above the stopping lane
-// means a predecessor has not published yet: poll again.
+// Tile-local part of the scan, shared by every tile a block processes: serial
+// scan of each run, wave scan of the run totals (exclusive result in wex), and
+// the (run, wave) totals left in LDS by lane 63, in element order.
 template <class Op>
-__device__ typename Op::T lookback_prefix(const uint64_t* status, int64_t tile, WsHeader* hdr)
+__device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[SCAN_CHUNKS],
+                                                typename Op::T (&wex)[SCAN_CHUNKS],
+                                                typename Op::T* s_part, int lane, int wave)
 {
     using T = typename Op::T;
-    const int lane = lane_id();
-    T excl = Op::identity();
-    int64_t last = tile - 1;
-    int spins = 0;
-    for (;;) {
-        const int64_t idx = last - 63 + lane;
-        const uint64_t w = (idx >= 0) ? status_load(status + idx) : pack32(ST_PREFIX, Op::identity());
-        const uint32_t flag = uint32_t(w >> 32);
-        const uint64_t empty = __ballot(flag == ST_EMPTY);
-        const uint64_t full = __ballot(flag == ST_PREFIX);
-        const int hi = full ? 63 - __builtin_clzll(full) : -1;
-        const uint64_t needed = (hi >= 0) ? (~0ull << hi) : ~0ull;
-        if (empty & needed) {
-            if (++spins < LOOKBACK_SPIN_LIMIT) {
-                __builtin_amdgcn_s_sleep(1);
-                continue;
-            }
-            if (lane == 0)
-                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
-            return excl;  // only reached on a defect; the error word reports it
-        }
-        const T v = (lane >= hi) ? from_bits<T>(uint32_t(w)) : Op::identity();
-        const T r = read_lane(wave_inclusive_scan<Op>(v), 63);
-        excl = Op::apply(r, excl);  // older tiles on the left
-        if (hi >= 0)
-            return excl;
-        last -= 64;
+#pragma unroll
+    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+        r[j].v[1] = Op::apply(r[j].v[0], r[j].v[1]);
+        r[j].v[2] = Op::apply(r[j].v[1], r[j].v[2]);
+        r[j].v[3] = Op::apply(r[j].v[2], r[j].v[3]);
+        const T inc = wave_inclusive_scan<Op>(r[j].v[3]);
+        wex[j] = wave_shift_up<Op>(inc);
+        if (lane == 63)
+            s_part[j * SCAN_WAVES + wave] = inc;
     }
 }
 
+#ifndef LS_SCAN_LDS_RESERVE
+#define LS_SCAN_LDS_RESERVE 0
+#endif
+
+// One tile per block; blocks take tile ids in the order they start.
 template <class Op, bool INCLUSIVE, bool VEC>
 __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     const typename Op::T* in, typename Op::T* out, int64_t n, int64_t num_tiles, WsHeader* hdr,
     uint64_t* status, typename Op::T* total)
 {
     using T = typename Op::T;
-    __shared__ T s_tot[SCAN_CHUNKS][SCAN_WAVES];
+    using Codec = ScanCodec<Op>;
+    constexpr int PARTS = SCAN_CHUNKS * SCAN_WAVES;  // (run, wave) partial totals per tile
+    constexpr uint32_t RUN_STRIDE = SCAN_BLOCK * 16u;
+    __shared__ T s_part[PARTS + LS_SCAN_LDS_RESERVE];
     __shared__ uint32_t s_tile;
-    __shared__ T s_prefix;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -95,63 +83,54 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     __syncthreads();
     const int64_t tile = s_tile;
     const int64_t tbase = tile * SCAN_TILE;
+    const int64_t rem = n - tbase;
+    const uint32_t valid = rem < SCAN_TILE ? uint32_t(rem) : uint32_t(SCAN_TILE);
+    const bool full = valid == SCAN_TILE;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + tbase, valid * 4u);
+    const uint32_t voff = uint32_t(tid) * 16u;  // run j of thread t: elements 4*(j*BLOCK + t) + 0..3
 
-    // 1. load: run j of thread t covers elements tbase + 4*(j*BLOCK + t) + 0..3
+    // 1. load.  Elements past n (last tile only) read as 0; they sit after every
+    // valid element in scan order, so no output below n depends on them.  The
+    // four element loads of a run are merged into one 128-bit access.
     Run4<T> r[SCAN_CHUNKS];
 #pragma unroll
     for (int j = 0; j < SCAN_CHUNKS; ++j)
-        r[j] = load_run<T, VEC>(in, tbase + 4 * int64_t(j * SCAN_BLOCK + tid), n, id);
+        r[j] = load_run_x1<T>(rin, voff, j * RUN_STRIDE);
 
-    // 2. serial inclusive scan of each run, then a wave scan of the run totals
+    // 2. local scan: runs, wave scan of run totals, (run, wave) totals to LDS
     T wex[SCAN_CHUNKS];
-#pragma unroll
-    for (int j = 0; j < SCAN_CHUNKS; ++j) {
-        r[j].v[1] = Op::apply(r[j].v[0], r[j].v[1]);
-        r[j].v[2] = Op::apply(r[j].v[1], r[j].v[2]);
-        r[j].v[3] = Op::apply(r[j].v[2], r[j].v[3]);
-        const T inc = wave_inclusive_scan<Op>(r[j].v[3]);
-        wex[j] = wave_shift_up<Op>(inc);
-        if (lane == 63)
-            s_tot[j][wave] = inc;
-    }
+    scan_tile_local<Op>(r, wex, s_part, lane, wave);
     __syncthreads();
 
-    // the (run, wave) totals in element order: run-major, then wave
-    T pre[SCAN_CHUNKS];
-    T agg = id;
-#pragma unroll
-    for (int jj = 0; jj < SCAN_CHUNKS; ++jj) {
-#pragma unroll
-        for (int ww = 0; ww < SCAN_WAVES; ++ww) {
-            if (ww == wave)
-                pre[jj] = agg;
-            agg = Op::apply(agg, s_tot[jj][ww]);
-        }
-    }
-
-    // 3. publish and look back
+    // 3. wave 0: scan the partial totals (one per lane), publish the tile total,
+    // look back for the tile prefix, and leave prefix (+) partial-exclusive in LDS.
     if (wave == 0) {
+        const T v = lane < PARTS ? s_part[lane] : id;
+        const T inc = wave_inclusive_scan<Op>(v);
+        const T exc = wave_shift_up<Op>(inc);
+        const T agg = read_lane(inc, 63);
         T p = id;
         if (tile == 0) {
             if (lane == 0)
-                status_store(status, pack32(ST_PREFIX, agg));
+                status_store(status, Codec::pack(ST_PREFIX, agg));
         } else {
             if (lane == 0)
-                status_store(status + tile, pack32(ST_AGGREGATE, agg));
-            p = lookback_prefix<Op>(status, tile, hdr);
+                status_store(status + tile, Codec::pack(ST_AGGREGATE, agg));
+            p = lookback<Codec>(status, tile, hdr);
             if (lane == 0)
-                status_store(status + tile, pack32(ST_PREFIX, Op::apply(p, agg)));
+                status_store(status + tile, Codec::pack(ST_PREFIX, Op::apply(p, agg)));
         }
-        if (lane == 0)
-            s_prefix = p;
+        if (lane < PARTS)
+            s_part[lane] = Op::apply(p, exc);
     }
     __syncthreads();
-    const T tp = s_prefix;
 
-    // 4. finish and store
+    // 4. finish and store; the thread holding element n-1 writes the total
+    const int64_t last_local = (tile == num_tiles - 1) ? int64_t(valid) - 1 : -1;
 #pragma unroll
     for (int j = 0; j < SCAN_CHUNKS; ++j) {
-        const T cp = Op::apply(tp, Op::apply(pre[j], wex[j]));
+        const T cp = Op::apply(s_part[j * SCAN_WAVES + wave], wex[j]);
         Run4<T> o;
         if constexpr (INCLUSIVE) {
 #pragma unroll
@@ -163,10 +142,23 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
             for (int k = 1; k < 4; ++k)
                 o.v[k] = Op::apply(cp, r[j].v[k - 1]);
         }
-        store_run<T, VEC>(out, tbase + 4 * int64_t(j * SCAN_BLOCK + tid), n, o);
+        if (VEC && full)
+            store_run_x4<T>(rout, voff, j * RUN_STRIDE, o);
+        else
+            store_run_x1<T>(rout, voff, j * RUN_STRIDE, o);
+        if (total != nullptr) {
+            // select, not index: a run-time index into r[] would move the whole
+            // tile from registers to per-lane scratch memory
+            const int64_t kk = last_local - 4 * int64_t(j * SCAN_BLOCK + tid);
+            if (kk >= 0 && kk < 4) {
+                T v = r[j].v[0];
+#pragma unroll
+                for (int k = 1; k < 4; ++k)
+                    v = (kk == k) ? r[j].v[k] : v;
+                *total = Op::apply(cp, v);
+            }
+        }
     }
-    if (total != nullptr && tile == num_tiles - 1 && tid == 0)
-        *total = Op::apply(tp, agg);
 }
 
 // Clears the workspace header and the first `words` status words.

@@ -15,9 +15,9 @@ from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 
 pytestmark = pytest.mark.gpu
 
-TILE = 4096
-SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 1023, 4095, 4096, 4097, 3 * TILE + 7, 64 * TILE,
-         70 * TILE + 1, 300_003]
+TILE = 8192  # the library's tile; sizes below also cover half and quarter tiles
+SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 1023, 4095, 4096, 4097, TILE - 1, TILE, TILE + 1,
+         3 * TILE + 7, 64 * TILE, 257 * TILE + 5, 300_003, 600 * TILE + 3]
 COMBOS = [("int32", "sum"), ("uint32", "sum"), ("int32", "max"), ("uint32", "max"),
           ("int32", "xor"), ("uint32", "xor"), ("float32", "sum"), ("float32", "max")]
 
@@ -96,7 +96,7 @@ def test_exact_float_special_case():
     """Integer-valued float32 data with all partial sums below 2^24 adds exactly in any
     order, so the GPU must match the oracle bit for bit there."""
     rng = np.random.default_rng(4)
-    x = rng.integers(-8, 9, 200 * TILE + 3).astype(np.float32)
+    x = rng.integers(-8, 9, 300 * TILE + 3).astype(np.float32)
     ref = oracle.scan(x, "sum", True)
     assert np.max(np.abs(ref.y)) < 2 ** 24
     got = to_host(ps.scan_inclusive(to_dev(x)))
