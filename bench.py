@@ -35,7 +35,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
-ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy")
+ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
+            "blockscans")
+DEFAULT_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
+                "blockscans")
 
 
 def log(msg):
@@ -95,7 +98,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default=",".join(ALL_LEGS))
+    ap.add_argument("--legs", default=",".join(DEFAULT_LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -216,6 +219,28 @@ def main():
         n = xs[0].numel()
         bw_leg("rows_2e16x1024_i32_excl", xs,
                lambda a, b: ps.batched_row_scan(a, "sum", True, out=b), n, 8 * n)
+        del xs
+    if "schemes" in legs:
+        # the three-phase device schemes on the headline workload (same bytes in and out)
+        n = wl.SIZES["big_scan"]
+        x = to_dev(wl.big_scan())
+        out = torch.empty_like(x)
+        for scheme, moved in (("reduce_then_scan", 3), ("scan_then_propagate", 4)):
+            ms = timer.run(lambda i, sc=scheme: ps.scan_ex(x, "sum", False, sc, out=out), K, W)
+            gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+            result_legs[f"scheme_{scheme}_i32_excl_2e28"] = {
+                "us": round(ms * 1e3, 1), "gelem_s": round(n / ms / 1e6, 1),
+                "algo_gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "bytes_moved_per_elem": 4 * moved}
+            log(f"scheme {scheme}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s (algorithmic)")
+        del x, out
+    if "blockscans" in legs:
+        # the block-level scan variants on 2^16 rows x 1024 int32 (one block per row)
+        xs = rotating(lambda i: to_dev(wl.rows1024()))
+        n = xs[0].numel()
+        for kind in ("wave_dpp", "hillis_steele", "hillis_steele_double", "blelloch"):
+            bw_leg(f"rows_2e16x1024_i32_excl_{kind}", xs,
+                   lambda a, b, k=kind: ps.batched_row_scan_ex(a, "sum", True, k, out=b), n, 8 * n)
         del xs
     if "copy" in legs:
         n = wl.SIZES["big_scan"]

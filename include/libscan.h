@@ -72,6 +72,43 @@ typedef enum ls_op { LS_SUM = 0, LS_MAX = 1, LS_XOR = 2 } ls_op;
  * type (signed, unsigned, or IEEE float with C semantics: NaN satisfies only NE). */
 typedef enum ls_cmp { LS_LT = 0, LS_LE = 1, LS_GT = 2, LS_GE = 3, LS_EQ = 4, LS_NE = 5 } ls_cmp;
 
+/* Device-wide schemes for scan_ex (the default entry points use the single pass).
+ *   LS_SCHEME_SINGLE_PASS          one launch; each tile publishes its total and
+ *                                  looks back over earlier tiles' published values
+ *                                  (the in-kernel hand-off through flags in global
+ *                                  memory that [Scan3] 四 mentions; [SIMT3] 5.1).
+ *                                  Moves 2*n*4 bytes.
+ *   LS_SCHEME_REDUCE_THEN_SCAN     tile totals, a scan of the totals, a seeded tile
+ *                                  scan: three launches, 3*n*4 bytes ([Scan3] 四).
+ *   LS_SCHEME_SCAN_THEN_PROPAGATE  tile scans with totals, a scan of the totals, an
+ *                                  offset pass over the output: 4*n*4 bytes
+ *                                  ([Scan3] 四, the three kernels as listed there).
+ * The three-phase schemes scan the tile totals recursively when they exceed one
+ * tile, as [Scan3] 四 describes for very large arrays. */
+typedef enum ls_scheme {
+    LS_SCHEME_SINGLE_PASS = 0,
+    LS_SCHEME_REDUCE_THEN_SCAN = 1,
+    LS_SCHEME_SCAN_THEN_PROPAGATE = 2
+} ls_scheme;
+
+/* Block-level scan used by batched_row_scan_ex for rows of more than 64 elements
+ * (one block of 256 threads per row, 4 elements per thread per 1024-element chunk).
+ *   LS_BLOCK_WAVE_DPP               64-lane DPP scans, wave totals through LDS, one
+ *                                   barrier ([Scan3] 五, the two-level block scan)
+ *   LS_BLOCK_HILLIS_STEELE          LDS Hillis-Steele, read / barrier / write /
+ *                                   barrier per step ([Scan3] 二)
+ *   LS_BLOCK_HILLIS_STEELE_DOUBLE   LDS Hillis-Steele with two buffers, one barrier
+ *                                   per step ([Scan3] 二)
+ *   LS_BLOCK_BLELLOCH               LDS up-sweep / down-sweep with padded indices
+ *                                   ([Scan3] 三; [SIMT3] 5.4)
+ * All four give identical results for integers and for max. */
+typedef enum ls_block_scan {
+    LS_BLOCK_WAVE_DPP = 0,
+    LS_BLOCK_HILLIS_STEELE = 1,
+    LS_BLOCK_HILLIS_STEELE_DOUBLE = 2,
+    LS_BLOCK_BLELLOCH = 3
+} ls_block_scan;
+
 /* Returns LS_ABI_VERSION of the loaded library. */
 int ls_abi_version(void);
 
@@ -94,14 +131,27 @@ ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t *bytes
  *   total     nullable; receives one element: the reduction of all n inputs,
  *             i.e. the value that no exclusive cell holds ([Scan3] 一).
  *   ws        device workspace of ws_bytes >= ls_scan_workspace_bytes(...),
- *             4-byte aligned (256-byte aligned is best).  Its contents on entry
- *             do not matter; the call re-initialises what it uses.
+ *             16-byte aligned (else LS_ERR_INVALID_ARG), not overlapping any
+ *             other argument.  Its contents on entry do not matter; the call
+ *             re-initialises what it uses.
  *   stream    hipStream_t as void*, or NULL.
  * One pass over the data: each element is read once and written once. */
 ls_status scan_inclusive(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, void *total,
                          void *ws, size_t ws_bytes, void *stream);
 ls_status scan_exclusive(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, void *total,
                          void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size for scan_ex with the given scheme (rules as above). */
+ls_status ls_scan_ex_workspace_bytes(int64_t n, ls_dtype t, ls_op op, ls_scheme scheme,
+                                     size_t *bytes);
+
+/* scan_inclusive / scan_exclusive with an explicit device-wide scheme.
+ *   exclusive  nonzero: exclusive scan; zero: inclusive.
+ *   scheme     see ls_scheme; an unknown value is LS_ERR_INVALID_ARG.
+ *   ws         at least ls_scan_ex_workspace_bytes(n, t, op, scheme) bytes.
+ * Other arguments, results and errors as for scan_inclusive. */
+ls_status scan_ex(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                  ls_scheme scheme, void *total, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace size for compact_if (same rules as ls_scan_workspace_bytes). */
 ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t *bytes);
@@ -132,6 +182,13 @@ ls_status compact_if(const void *in, void *out, int64_t *count, int64_t n, ls_dt
  * Needs no workspace. */
 ls_status batched_row_scan(const void *in, void *out, int64_t rows, int64_t cols, ls_dtype t,
                            ls_op op, int exclusive, void *stream);
+
+/* batched_row_scan with an explicit block-level scan for the one-block-per-row
+ * path (see ls_block_scan); with LS_BLOCK_WAVE_DPP it is batched_row_scan.  Other
+ * kinds run rows of any length through that path.  An unknown kind is
+ * LS_ERR_INVALID_ARG. */
+ls_status batched_row_scan_ex(const void *in, void *out, int64_t rows, int64_t cols, ls_dtype t,
+                              ls_op op, int exclusive, ls_block_scan block_scan, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "LibscanError", "library_path", "load_library", "ls_abi_version", "ls_status_string",
     "ls_scan_workspace_bytes", "ls_compact_workspace_bytes", "scan_inclusive", "scan_exclusive",
-    "compact_if", "batched_row_scan", "workspace_for",
+    "compact_if", "batched_row_scan", "workspace_for", "scan_ex", "ls_scan_ex_workspace_bytes",
+    "batched_row_scan_ex",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,8 @@ LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = ra
 DTYPE_CODES = {"int32": 0, "uint32": 1, "float32": 2}
 OP_CODES = {"sum": 0, "max": 1, "xor": 2}
 CMP_CODES = {"lt": 0, "le": 1, "gt": 2, "ge": 3, "eq": 4, "ne": 5}
+SCHEME_CODES = {"single_pass": 0, "reduce_then_scan": 1, "scan_then_propagate": 2}
+BLOCK_SCAN_CODES = {"wave_dpp": 0, "hillis_steele": 1, "hillis_steele_double": 2, "blelloch": 3}
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "float32"}
 if hasattr(torch, "uint32"):
     _TORCH_DTYPES[torch.uint32] = "uint32"
@@ -75,6 +78,12 @@ def load_library():
             fn = getattr(lib, name)
             fn.argtypes = [P, P, I64, I, I, P, P, SZ, P]
             fn.restype = I
+        lib.ls_scan_ex_workspace_bytes.argtypes = [I64, I, I, I, ctypes.POINTER(SZ)]
+        lib.ls_scan_ex_workspace_bytes.restype = I
+        lib.scan_ex.argtypes = [P, P, I64, I, I, I, I, P, P, SZ, P]
+        lib.scan_ex.restype = I
+        lib.batched_row_scan_ex.argtypes = [P, P, I64, I64, I, I, I, I, P]
+        lib.batched_row_scan_ex.restype = I
         lib.compact_if.argtypes = [P, P, P, I64, I, I, U32, P, SZ, P]
         lib.compact_if.restype = I
         lib.batched_row_scan.argtypes = [P, P, I64, I64, I, I, I, P]
@@ -100,6 +109,14 @@ def ls_scan_workspace_bytes(n: int, dtype: str, op: str) -> int:
     out = ctypes.c_size_t(0)
     _check(load_library().ls_scan_workspace_bytes(n, DTYPE_CODES[dtype], OP_CODES[op],
                                                   ctypes.byref(out)), "ls_scan_workspace_bytes")
+    return out.value
+
+
+def ls_scan_ex_workspace_bytes(n: int, dtype: str, op: str, scheme: str) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ls_scan_ex_workspace_bytes(n, DTYPE_CODES[dtype], OP_CODES[op],
+                                                     SCHEME_CODES[scheme], ctypes.byref(out)),
+           "ls_scan_ex_workspace_bytes")
     return out.value
 
 
@@ -185,6 +202,32 @@ def scan_exclusive(x: torch.Tensor, op: str = "sum", out: torch.Tensor | None = 
     return _scan("scan_exclusive", x, op, out, total)
 
 
+def scan_ex(x: torch.Tensor, op: str = "sum", inclusive: bool = True,
+            scheme: str = "single_pass", out: torch.Tensor | None = None,
+            total: torch.Tensor | None = None) -> torch.Tensor:
+    """A scan with an explicit device-wide scheme: "single_pass",
+    "reduce_then_scan" or "scan_then_propagate" (see ls_scheme in libscan.h)."""
+    lib = load_library()
+    _require_gpu(x, out, total)
+    if not x.is_contiguous():
+        raise ValueError("libscan: input must be contiguous")
+    dt = _dtype_of(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
+        raise ValueError("libscan: out must be a contiguous tensor like the input")
+    if total is not None and (total.dtype != x.dtype or total.numel() < 1):
+        raise ValueError("libscan: total must hold one element of the input dtype")
+    n = x.numel()
+    stream, sh = _stream_handle(x.device)
+    need = ls_scan_ex_workspace_bytes(n, dt, op, scheme)
+    ws = workspace_for(x.device, stream, need)
+    st = lib.scan_ex(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], 0 if inclusive else 1,
+                     SCHEME_CODES[scheme], _ptr(total), _ptr(ws), ws.numel(), sh)
+    _check(st, "scan_ex")
+    return out
+
+
 def compact_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | None = None,
                count: torch.Tensor | None = None):
     """Stable compaction of the flattened x under (x CMP threshold).
@@ -229,4 +272,23 @@ def batched_row_scan(x: torch.Tensor, op: str = "sum", exclusive: bool = True,
     st = lib.batched_row_scan(_ptr(x), _ptr(out), rows, cols, DTYPE_CODES[dt], OP_CODES[op],
                               1 if exclusive else 0, sh)
     _check(st, "batched_row_scan")
+    return out
+
+
+def batched_row_scan_ex(x: torch.Tensor, op: str = "sum", exclusive: bool = True,
+                        block_scan: str = "wave_dpp", out: torch.Tensor | None = None) -> torch.Tensor:
+    """batched_row_scan with an explicit block-level scan: "wave_dpp",
+    "hillis_steele", "hillis_steele_double" or "blelloch" (see ls_block_scan)."""
+    lib = load_library()
+    _require_gpu(x, out)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("libscan: batched_row_scan wants a contiguous 2-D tensor")
+    dt = _dtype_of(x)
+    if out is None:
+        out = torch.empty_like(x)
+    rows, cols = x.shape
+    _, sh = _stream_handle(x.device)
+    st = lib.batched_row_scan_ex(_ptr(x), _ptr(out), rows, cols, DTYPE_CODES[dt], OP_CODES[op],
+                                 1 if exclusive else 0, BLOCK_SCAN_CODES[block_scan], sh)
+    _check(st, "batched_row_scan_ex")
     return out

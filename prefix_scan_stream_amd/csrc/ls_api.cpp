@@ -14,6 +14,8 @@ namespace {
 bool valid_dtype(ls_dtype t) { return t == LS_INT32 || t == LS_UINT32 || t == LS_FLOAT32; }
 bool valid_op(ls_op op) { return op == LS_SUM || op == LS_MAX || op == LS_XOR; }
 bool valid_cmp(ls_cmp c) { return c >= LS_LT && c <= LS_NE; }
+bool valid_scheme(ls_scheme c) { return c >= LS_SCHEME_SINGLE_PASS && c <= LS_SCHEME_SCAN_THEN_PROPAGATE; }
+bool valid_block_scan(ls_block_scan c) { return c >= LS_BLOCK_WAVE_DPP && c <= LS_BLOCK_BLELLOCH; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -39,9 +41,9 @@ ls_status check_ws(const void* ws, size_t ws_bytes, size_t need)
 }
 
 ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
-                      void* ws, size_t ws_bytes, void* stream, bool inclusive)
+                      void* ws, size_t ws_bytes, void* stream, bool inclusive, ls_scheme scheme)
 {
-    if (!size_ok(n) || !valid_dtype(t) || !valid_op(op))
+    if (!size_ok(n) || !valid_dtype(t) || !valid_op(op) || !valid_scheme(scheme))
         return LS_ERR_INVALID_ARG;
     const size_t bytes = size_t(n) * 4;
     if (n > 0) {
@@ -56,14 +58,14 @@ ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op
     }
     if (t == LS_FLOAT32 && op == LS_XOR)
         return LS_ERR_UNSUPPORTED;
-    const size_t need = ls::scan_workspace_bytes(n);
+    const size_t need = ls::scan_workspace_bytes(n, int(scheme));
     ls_status st = check_ws(ws, ws_bytes, need);
     if (st != LS_OK)
         return st;
     if (!aligned(ws, 16) || overlaps(ws, need, in, bytes) || overlaps(ws, need, out, bytes) ||
         (total != nullptr && overlaps(ws, need, total, 4)))
         return LS_ERR_INVALID_ARG;
-    return from_hip(ls::launch_scan(in, out, n, int(t), int(op), inclusive, total, ws,
+    return from_hip(ls::launch_scan(in, out, n, int(t), int(op), inclusive, total, ws, int(scheme),
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -91,20 +93,36 @@ ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t* bytes
         return LS_ERR_INVALID_ARG;
     if (t == LS_FLOAT32 && op == LS_XOR)
         return LS_ERR_UNSUPPORTED;
-    *bytes = ls::scan_workspace_bytes(n);
+    *bytes = ls::scan_workspace_bytes(n, ls::SCHEME_SINGLE_PASS);
+    return LS_OK;
+}
+
+ls_status ls_scan_ex_workspace_bytes(int64_t n, ls_dtype t, ls_op op, ls_scheme scheme, size_t* bytes)
+{
+    if (bytes == nullptr || !size_ok(n) || !valid_dtype(t) || !valid_op(op) || !valid_scheme(scheme))
+        return LS_ERR_INVALID_ARG;
+    if (t == LS_FLOAT32 && op == LS_XOR)
+        return LS_ERR_UNSUPPORTED;
+    *bytes = ls::scan_workspace_bytes(n, int(scheme));
     return LS_OK;
 }
 
 ls_status scan_inclusive(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
                          void* ws, size_t ws_bytes, void* stream)
 {
-    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, true);
+    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, true, LS_SCHEME_SINGLE_PASS);
 }
 
 ls_status scan_exclusive(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
                          void* ws, size_t ws_bytes, void* stream)
 {
-    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, false);
+    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, false, LS_SCHEME_SINGLE_PASS);
+}
+
+ls_status scan_ex(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                  ls_scheme scheme, void* total, void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, exclusive == 0, scheme);
 }
 
 ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t* bytes)
@@ -140,10 +158,10 @@ ls_status compact_if(const void* in, void* out, int64_t* count, int64_t n, ls_dt
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
-ls_status batched_row_scan(const void* in, void* out, int64_t rows, int64_t cols, ls_dtype t,
-                           ls_op op, int exclusive, void* stream)
+static ls_status batched_common(const void* in, void* out, int64_t rows, int64_t cols, ls_dtype t,
+                                ls_op op, int exclusive, ls_block_scan kind, void* stream)
 {
-    if (rows < 0 || cols < 0 || !valid_dtype(t) || !valid_op(op))
+    if (rows < 0 || cols < 0 || !valid_dtype(t) || !valid_op(op) || !valid_block_scan(kind))
         return LS_ERR_INVALID_ARG;
     if (rows > 0 && cols > INT64_MAX / 8 / rows)
         return LS_ERR_INVALID_ARG;
@@ -157,8 +175,20 @@ ls_status batched_row_scan(const void* in, void* out, int64_t rows, int64_t cols
     }
     if (t == LS_FLOAT32 && op == LS_XOR)
         return LS_ERR_UNSUPPORTED;
-    return from_hip(ls::launch_batched(in, out, rows, cols, int(t), int(op), exclusive != 0,
+    return from_hip(ls::launch_batched(in, out, rows, cols, int(t), int(op), exclusive != 0, int(kind),
                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+ls_status batched_row_scan(const void* in, void* out, int64_t rows, int64_t cols, ls_dtype t,
+                           ls_op op, int exclusive, void* stream)
+{
+    return batched_common(in, out, rows, cols, t, op, exclusive, LS_BLOCK_WAVE_DPP, stream);
+}
+
+ls_status batched_row_scan_ex(const void* in, void* out, int64_t rows, int64_t cols, ls_dtype t,
+                              ls_op op, int exclusive, ls_block_scan block_scan, void* stream)
+{
+    return batched_common(in, out, rows, cols, t, op, exclusive, block_scan, stream);
 }
 
 }  // extern "C"

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
     uint32_t keep[CP_CHUNKS];  // bit k: element k of the run is kept
 #pragma unroll
     for (int j = 0; j < CP_CHUNKS; ++j)
-        r[j] = load_run_x1<uint32_t>(rin, voff, j * RUN_STRIDE);
+        r[j] = VEC ? load_run_x4<uint32_t>(rin, voff, j * RUN_STRIDE)
+                   : load_run_x1<uint32_t>(rin, voff, j * RUN_STRIDE);
 #pragma unroll
     for (int j = 0; j < CP_CHUNKS; ++j) {
         const uint32_t e0 = 4u * uint32_t(j * CP_BLOCK + tid);

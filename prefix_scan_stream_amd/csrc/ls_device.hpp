@@ -157,7 +157,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), BUF_DWORD3);
 }
 
-// One 128-bit access (base and offsets 16-byte aligned, run fully in range).
+// One 128-bit access (base and offsets 16-byte aligned).  The range check of a
+// raw buffer access applies to each 32-bit word, so a run that straddles the end
+// of the window returns its in-range words and 0 for the rest.
 template <class T>
 __device__ __forceinline__ Run4<T> load_run_x4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff)
 {

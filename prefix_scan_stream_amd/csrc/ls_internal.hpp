@@ -11,14 +11,16 @@ namespace ls {
 // Element-type and operator codes (the values of ls_dtype / ls_op / ls_cmp).
 enum Dtype : int { DT_INT32 = 0, DT_UINT32 = 1, DT_FLOAT32 = 2 };
 enum OpCode : int { OP_SUM = 0, OP_MAX = 1, OP_XOR = 2 };
+// Device-wide schemes (the values of ls_scheme).
+enum Scheme : int { SCHEME_SINGLE_PASS = 0, SCHEME_REDUCE_THEN_SCAN = 1, SCHEME_SCAN_THEN_PROPAGATE = 2 };
 
 // ---- single-pass device-wide scan (ls_scan.hip)
 // Zeroes the workspace header and `status_words` tile status words after it.
 hipError_t clear_workspace(void* ws, int64_t status_words, hipStream_t stream);
 int64_t scan_tile_elems();
-size_t scan_workspace_bytes(int64_t n);
+size_t scan_workspace_bytes(int64_t n, int scheme);
 hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, bool inclusive,
-                       void* total, void* ws, hipStream_t stream);
+                       void* total, void* ws, int scheme, hipStream_t stream);
 
 // ---- fused compaction (ls_compact.hip)
 int64_t compact_tile_elems();
@@ -27,7 +29,8 @@ hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, 
                           uint32_t threshold_bits, void* ws, hipStream_t stream);
 
 // ---- batched row scan (ls_batched.hip)
+// kind: the block-level scan (ls_block_scan values); 0 = wave DPP, the default.
 hipError_t launch_batched(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int op,
-                          bool exclusive, hipStream_t stream);
+                          bool exclusive, int kind, hipStream_t stream);
 
 }  // namespace ls

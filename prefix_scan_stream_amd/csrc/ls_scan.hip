@@ -90,13 +90,13 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + tbase, valid * 4u);
     const uint32_t voff = uint32_t(tid) * 16u;  // run j of thread t: elements 4*(j*BLOCK + t) + 0..3
 
-    // 1. load.  Elements past n (last tile only) read as 0; they sit after every
-    // valid element in scan order, so no output below n depends on them.  The
-    // four element loads of a run are merged into one 128-bit access.
+    // 1. load.  Elements past n (last tile only) read as 0 (the buffer range is
+    // checked per 32-bit word); they sit after every valid element in scan order,
+    // so no output below n depends on them.
     Run4<T> r[SCAN_CHUNKS];
 #pragma unroll
     for (int j = 0; j < SCAN_CHUNKS; ++j)
-        r[j] = load_run_x1<T>(rin, voff, j * RUN_STRIDE);
+        r[j] = VEC ? load_run_x4<T>(rin, voff, j * RUN_STRIDE) : load_run_x1<T>(rin, voff, j * RUN_STRIDE);
 
     // 2. local scan: runs, wave scan of run totals, (run, wave) totals to LDS
     T wex[SCAN_CHUNKS];
@@ -161,6 +161,162 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     }
 }
 
+// ---------------------------------------------------------------- three-phase
+// The multi-block composition of the parallel prefix scan page (geek-doc.cn,
+// section 四): scan each block, scan the block totals, add each block's offset.
+// Kept beside the single pass so the two can be measured against each other.
+//   reduce-then-scan   tile totals (read n) -> scan of totals -> seeded tile scan
+//                      (read n, write n): 3n*4 bytes;
+//   scan-then-propagate local tile scans + totals (read n, write n) -> scan of
+//                      totals -> offsets added in place (read n, write n): 4n*4.
+// No tile waits for another, so no status words and no tile counter; elements
+// past n are replaced by the identity so every tile total is exact.
+
+// Tile total: serial per thread over its runs, wave reduce, LDS across waves.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(SCAN_BLOCK) void tile_reduce_kernel(const typename Op::T* in, int64_t n,
+                                                                 typename Op::T* totals)
+{
+    using T = typename Op::T;
+    __shared__ T s_w[SCAN_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t tile = blockIdx.x;
+    const int64_t rem = n - tile * SCAN_TILE;
+    const uint32_t valid = rem < SCAN_TILE ? uint32_t(rem) : uint32_t(SCAN_TILE);
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tile * SCAN_TILE, valid * 4u);
+    const uint32_t voff = uint32_t(tid) * 16u;
+    T acc = Op::identity();
+#pragma unroll
+    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+        const Run4<T> r = VEC ? load_run_x4<T>(rin, voff, j * SCAN_BLOCK * 16u)
+                              : load_run_x1<T>(rin, voff, j * SCAN_BLOCK * 16u);
+        const uint32_t e0 = 4u * uint32_t(j * SCAN_BLOCK + tid);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            acc = Op::apply(acc, e0 + k < valid ? r.v[k] : Op::identity());
+    }
+    const T inc = wave_inclusive_scan<Op>(acc);
+    if (lane == 63)
+        s_w[wave] = inc;
+    __syncthreads();
+    if (tid == 0) {
+        T t = Op::identity();
+#pragma unroll
+        for (int w = 0; w < SCAN_WAVES; ++w)
+            t = Op::apply(t, s_w[w]);
+        totals[tile] = t;
+    }
+}
+
+// Tile scan with a given tile prefix: seeds[tile] when seeds != nullptr, else
+// the identity; writes the tile total to totals[tile] when totals != nullptr.
+template <class Op, bool INCLUSIVE, bool VEC>
+__global__ __launch_bounds__(SCAN_BLOCK) void tile_scan_kernel(const typename Op::T* in,
+                                                               typename Op::T* out, int64_t n,
+                                                               const typename Op::T* seeds,
+                                                               typename Op::T* totals)
+{
+    using T = typename Op::T;
+    constexpr int PARTS = SCAN_CHUNKS * SCAN_WAVES;
+    constexpr uint32_t RUN_STRIDE = SCAN_BLOCK * 16u;
+    __shared__ T s_part[PARTS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const T id = Op::identity();
+    const int64_t tile = blockIdx.x;
+    const int64_t tbase = tile * SCAN_TILE;
+    const int64_t rem = n - tbase;
+    const uint32_t valid = rem < SCAN_TILE ? uint32_t(rem) : uint32_t(SCAN_TILE);
+    const bool full = valid == SCAN_TILE;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + tbase, valid * 4u);
+    const uint32_t voff = uint32_t(tid) * 16u;
+
+    Run4<T> r[SCAN_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+        r[j] = VEC ? load_run_x4<T>(rin, voff, j * RUN_STRIDE) : load_run_x1<T>(rin, voff, j * RUN_STRIDE);
+        if (!full) {
+            const uint32_t e0 = 4u * uint32_t(j * SCAN_BLOCK + tid);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                r[j].v[k] = e0 + k < valid ? r[j].v[k] : id;
+        }
+    }
+    T wex[SCAN_CHUNKS];
+    scan_tile_local<Op>(r, wex, s_part, lane, wave);
+    __syncthreads();
+    if (wave == 0) {
+        const T v = lane < PARTS ? s_part[lane] : id;
+        const T inc = wave_inclusive_scan<Op>(v);
+        const T exc = wave_shift_up<Op>(inc);
+        const T p = seeds != nullptr ? seeds[tile] : id;
+        if (totals != nullptr && lane == 0)
+            totals[tile] = read_lane(inc, 63);
+        if (lane < PARTS)
+            s_part[lane] = Op::apply(p, exc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+        const T cp = Op::apply(s_part[j * SCAN_WAVES + wave], wex[j]);
+        Run4<T> o;
+        if constexpr (INCLUSIVE) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o.v[k] = Op::apply(cp, r[j].v[k]);
+        } else {
+            o.v[0] = cp;
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+                o.v[k] = Op::apply(cp, r[j].v[k - 1]);
+        }
+        if (VEC && full)
+            store_run_x4<T>(rout, voff, j * RUN_STRIDE, o);
+        else
+            store_run_x1<T>(rout, voff, j * RUN_STRIDE, o);
+    }
+}
+
+// out[i] = seeds[tile] (+) out[i] over each tile, in place.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(SCAN_BLOCK) void add_offset_kernel(typename Op::T* out, int64_t n,
+                                                                const typename Op::T* seeds)
+{
+    using T = typename Op::T;
+    constexpr uint32_t RUN_STRIDE = SCAN_BLOCK * 16u;
+    const int64_t tile = blockIdx.x;
+    const int64_t tbase = tile * SCAN_TILE;
+    const int64_t rem = n - tbase;
+    const uint32_t valid = rem < SCAN_TILE ? uint32_t(rem) : uint32_t(SCAN_TILE);
+    const bool full = valid == SCAN_TILE;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(out + tbase, valid * 4u);
+    const uint32_t voff = uint32_t(threadIdx.x) * 16u;
+    const T p = seeds[tile];
+    Run4<T> r[SCAN_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < SCAN_CHUNKS; ++j)
+        r[j] = VEC ? load_run_x4<T>(rs, voff, j * RUN_STRIDE) : load_run_x1<T>(rs, voff, j * RUN_STRIDE);
+#pragma unroll
+    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            r[j].v[k] = Op::apply(p, r[j].v[k]);
+        if (VEC && full)
+            store_run_x4<T>(rs, voff, j * RUN_STRIDE, r[j]);
+        else
+            store_run_x1<T>(rs, voff, j * RUN_STRIDE, r[j]);
+    }
+}
+
+// total = seeds[last] (+) totals[last]
+template <class Op>
+__global__ void write_total_kernel(const typename Op::T* seeds, const typename Op::T* totals,
+                                   int64_t last, typename Op::T* total)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0)
+        *total = Op::apply(seeds[last], totals[last]);
+}
+
 // Clears the workspace header and the first `words` status words.
 __global__ __launch_bounds__(256) void ws_clear_kernel(uint4* p, int64_t n16)
 {
@@ -181,13 +337,23 @@ int64_t scan_tile_elems() { return SCAN_TILE; }
 
 static int64_t num_tiles_for(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
 
-size_t scan_workspace_bytes(int64_t n)
+static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Single pass: header + one status word per tile.  Three-phase: tile totals and
+// their scan (seeds), plus, when the totals span more than one tile, the
+// workspace of the same scheme over the totals (the recursion of the page's
+// multi-level scan).
+size_t scan_workspace_bytes(int64_t n, int scheme)
 {
     int64_t tiles = num_tiles_for(n);
     if (tiles < 1)
         tiles = 1;
-    size_t bytes = sizeof(WsHeader) + size_t(tiles) * sizeof(uint64_t);
-    return (bytes + 255) & ~size_t(255);
+    if (scheme == SCHEME_SINGLE_PASS)
+        return round256(sizeof(WsHeader) + size_t(tiles) * sizeof(uint64_t));
+    size_t bytes = 2 * round256(size_t(tiles) * 4);
+    if (tiles > SCAN_TILE)
+        bytes += scan_workspace_bytes(tiles, scheme);
+    return bytes;
 }
 
 hipError_t clear_workspace(void* ws, int64_t status_words, hipStream_t s)
@@ -249,22 +415,106 @@ static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive,
     return hipGetLastError();
 }
 
+template <class Op>
+static hipError_t run_three_phase(const typename Op::T* in, typename Op::T* out, int64_t n,
+                                  bool inclusive, typename Op::T* total, char* ws, int scheme,
+                                  hipStream_t s);
+
+// Exclusive scan of the m tile totals into seeds: one block when they fit a
+// tile, else the same scheme again over the totals.
+template <class Op>
+static hipError_t scan_totals(const typename Op::T* totals, typename Op::T* seeds, int64_t m,
+                              char* sub_ws, int scheme, hipStream_t s)
+{
+    if (m <= SCAN_TILE) {
+        hipLaunchKernelGGL((tile_scan_kernel<Op, false, true>), dim3(1), dim3(SCAN_BLOCK), 0, s,
+                           totals, seeds, m, static_cast<const typename Op::T*>(nullptr),
+                           static_cast<typename Op::T*>(nullptr));
+        return hipGetLastError();
+    }
+    return run_three_phase<Op>(totals, seeds, m, false, nullptr, sub_ws, scheme, s);
+}
+
+template <class Op, bool INCLUSIVE>
+static void launch_tile_scan(bool vec, const typename Op::T* in, typename Op::T* out, int64_t n,
+                             int64_t tiles, const typename Op::T* seeds, typename Op::T* totals,
+                             hipStream_t s)
+{
+    const dim3 grid(static_cast<uint32_t>(tiles)), block(SCAN_BLOCK);
+    if (vec)
+        hipLaunchKernelGGL((tile_scan_kernel<Op, INCLUSIVE, true>), grid, block, 0, s, in, out, n, seeds, totals);
+    else
+        hipLaunchKernelGGL((tile_scan_kernel<Op, INCLUSIVE, false>), grid, block, 0, s, in, out, n, seeds, totals);
+}
+
+template <class Op>
+static hipError_t run_three_phase(const typename Op::T* in, typename Op::T* out, int64_t n,
+                                  bool inclusive, typename Op::T* total, char* ws, int scheme,
+                                  hipStream_t s)
+{
+    using T = typename Op::T;
+    const int64_t tiles = num_tiles_for(n);
+    T* totals = reinterpret_cast<T*>(ws);
+    T* seeds = reinterpret_cast<T*>(ws + round256(size_t(tiles) * 4));
+    char* sub = ws + 2 * round256(size_t(tiles) * 4);
+    const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+    const dim3 grid(static_cast<uint32_t>(tiles)), block(SCAN_BLOCK);
+    hipError_t e;
+    if (scheme == SCHEME_REDUCE_THEN_SCAN) {
+        if (((reinterpret_cast<uintptr_t>(in)) & 15) == 0)
+            hipLaunchKernelGGL((tile_reduce_kernel<Op, true>), grid, block, 0, s, in, n, totals);
+        else
+            hipLaunchKernelGGL((tile_reduce_kernel<Op, false>), grid, block, 0, s, in, n, totals);
+        if ((e = scan_totals<Op>(totals, seeds, tiles, sub, scheme, s)) != hipSuccess)
+            return e;
+        if (inclusive)
+            launch_tile_scan<Op, true>(vec, in, out, n, tiles, seeds, nullptr, s);
+        else
+            launch_tile_scan<Op, false>(vec, in, out, n, tiles, seeds, nullptr, s);
+    } else {
+        if (inclusive)
+            launch_tile_scan<Op, true>(vec, in, out, n, tiles, nullptr, totals, s);
+        else
+            launch_tile_scan<Op, false>(vec, in, out, n, tiles, nullptr, totals, s);
+        if ((e = scan_totals<Op>(totals, seeds, tiles, sub, scheme, s)) != hipSuccess)
+            return e;
+        if (((reinterpret_cast<uintptr_t>(out)) & 15) == 0)
+            hipLaunchKernelGGL((add_offset_kernel<Op, true>), grid, block, 0, s, out, n, seeds);
+        else
+            hipLaunchKernelGGL((add_offset_kernel<Op, false>), grid, block, 0, s, out, n, seeds);
+    }
+    if (total != nullptr)
+        hipLaunchKernelGGL((write_total_kernel<Op>), dim3(1), dim3(64), 0, s, seeds, totals, tiles - 1, total);
+    return hipGetLastError();
+}
+
+template <class Op>
+static hipError_t run_scan_scheme(const void* in, void* out, int64_t n, bool inclusive, void* total,
+                                  void* ws, int scheme, hipStream_t s)
+{
+    using T = typename Op::T;
+    if (scheme == SCHEME_SINGLE_PASS || n == 0)
+        return run_scan<Op>(in, out, n, inclusive, total, ws, s);
+    return run_three_phase<Op>(reinterpret_cast<const T*>(in), reinterpret_cast<T*>(out), n, inclusive,
+                               reinterpret_cast<T*>(total), reinterpret_cast<char*>(ws), scheme, s);
+}
+
 hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, bool inclusive,
-                       void* total, void* ws, hipStream_t s)
+                       void* total, void* ws, int scheme, hipStream_t s)
 {
     switch (op) {
     case OP_SUM:
         if (dtype == DT_FLOAT32)
-            return run_scan<SumF32>(in, out, n, inclusive, total, ws, s);
-        return run_scan<SumU32>(in, out, n, inclusive, total, ws, s);
+            return run_scan_scheme<SumF32>(in, out, n, inclusive, total, ws, scheme, s);
+        return run_scan_scheme<SumU32>(in, out, n, inclusive, total, ws, scheme, s);
     case OP_XOR:
-        return run_scan<XorU32>(in, out, n, inclusive, total, ws, s);
+        return run_scan_scheme<XorU32>(in, out, n, inclusive, total, ws, scheme, s);
     case OP_MAX:
         if (dtype == DT_INT32)
-            return run_scan<MaxI32>(in, out, n, inclusive, total, ws, s);
+            return run_scan_scheme<MaxI32>(in, out, n, inclusive, total, ws, scheme, s);
         if (dtype == DT_UINT32)
-            return run_scan<MaxU32>(in, out, n, inclusive, total, ws, s);
-        return run_scan<MaxF32>(in, out, n, inclusive, total, ws, s);
+            return run_scan_scheme<MaxU32>(in, out, n, inclusive, total, ws, scheme, s);
+        return run_scan_scheme<MaxF32>(in, out, n, inclusive, total, ws, scheme, s);
     }
     return hipErrorInvalidValue;
 }

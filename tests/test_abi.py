@@ -108,6 +108,36 @@ def test_scan_validation(lib, fn):
     assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=XOR, ws=None) == UNS
 
 
+def test_extended_entry_points_validation(lib):
+    sz = ctypes.c_size_t(0)
+    for scheme in range(3):
+        assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, scheme, ctypes.byref(sz)) == 0
+        assert sz.value > 0
+    assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, 3, ctypes.byref(sz)) == INV
+    assert lib.ls_scan_ex_workspace_bytes(10, F32, XOR, 1, ctypes.byref(sz)) == UNS
+    # three-phase workspaces grow with the recursion over the tile totals
+    assert ps.ls_scan_ex_workspace_bytes(1 << 34, "int32", "sum", "reduce_then_scan") > \
+        2 * 4 * ((1 << 34) // (1 << 14))
+
+    def sx(scheme=0, n=10, ws=A_WS, wsb=BIG_WS, t=INT32, op=SUM, excl=1):
+        return lib.scan_ex(A_IN, A_OUT, n, t, op, excl, scheme, None, ws, wsb, None)
+
+    assert sx(scheme=3) == INV
+    assert sx(scheme=-1) == INV
+    assert sx(scheme=1, n=-2) == INV
+    assert sx(scheme=2, t=F32, op=XOR) == UNS
+    assert sx(scheme=1, ws=None) == WS
+    assert sx(scheme=2, n=1 << 24, wsb=256) == WS
+
+    def bx(kind=0, rows=4, cols=100):
+        return lib.batched_row_scan_ex(A_IN, A_OUT, rows, cols, INT32, SUM, 1, kind, None)
+
+    assert bx(kind=4) == INV
+    assert bx(kind=-1) == INV
+    assert bx(kind=3, rows=-1) == INV
+    assert lib.batched_row_scan_ex(None, None, 0, 5, INT32, SUM, 1, 2, None) == ps.LS_OK
+
+
 def test_compact_validation(lib):
     def call(inp=A_IN, out=A_OUT, count=A_TOT, n=10, t=INT32, cmp=0, ws=A_WS, wsb=BIG_WS):
         return lib.compact_if(inp, out, count, n, t, cmp, 5, ws, wsb, None)

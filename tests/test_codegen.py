@@ -56,3 +56,30 @@ def test_status_words_use_device_coherent_accesses(asm):
     text = asm["ls_scan.hip"]
     assert re.search(r"global_load_dwordx2 .* sc1", text)
     assert re.search(r"global_store_dwordx2 .* sc1", text)
+
+
+def kernel_body(text, mangled_prefix):
+    """Assembly of the first kernel whose symbol starts with mangled_prefix."""
+    lines = text.split("\n")
+    for i, line in enumerate(lines):
+        if line.startswith(mangled_prefix) and line.split(";")[0].rstrip().endswith(":"):
+            body = []
+            for l2 in lines[i + 1:]:
+                body.append(l2)
+                if "s_endpgm" in l2:
+                    return "\n".join(body)
+    raise AssertionError(f"kernel {mangled_prefix} not found")
+
+
+@pytest.mark.parametrize("src,prefix", [
+    ("ls_scan.hip", "_ZN2ls23scan_single_pass_kernelINS_6SumU32ELb0ELb1E"),
+    ("ls_scan.hip", "_ZN2ls18tile_reduce_kernelINS_6SumU32ELb1E"),
+    ("ls_scan.hip", "_ZN2ls16tile_scan_kernelINS_6SumU32ELb0ELb1E"),
+    ("ls_scan.hip", "_ZN2ls17add_offset_kernelINS_6SumU32ELb1E"),
+    ("ls_compact.hip", "_ZN2ls14compact_kernelILi0ELb1E"),
+])
+def test_aligned_tiles_load_128_bits(asm, src, prefix):
+    """Aligned tiles are read with 128-bit loads only (one per run of 4)."""
+    body = kernel_body(asm[src], prefix)
+    assert len(re.findall(r"buffer_load_dwordx4", body)) >= 16
+    assert not re.search(r"buffer_load_dword\s", body)

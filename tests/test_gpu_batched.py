@@ -64,3 +64,34 @@ def test_rows64_workload():
 def test_rows1024_workload():
     """2^16 rows x 1024 int32, values U{0..9}: bit-exact, every element."""
     check_batched(wl.rows1024(), "sum", True)
+
+
+BLOCK_SCANS = ["wave_dpp", "hillis_steele", "hillis_steele_double", "blelloch"]
+
+
+def check_variant(x2, op, exclusive, kind):
+    ref = oracle.batched(x2, op, inclusive=not exclusive)
+    got = to_host(ps.batched_row_scan_ex(to_dev(x2), op, exclusive, kind))
+    if str(x2.dtype) == "float32" and op == "sum":
+        ok, worst, k = oracle.fp32_sum_within_tolerance(got, ref)
+        assert ok, f"{kind}: ratio {worst:.3g} at flat index {k}"
+    else:
+        mism = np.flatnonzero(bits(got).reshape(-1) != bits(ref.y).reshape(-1))
+        assert mism.size == 0, f"{kind}: {mism.size} mismatches, first at flat index {mism[0]}"
+
+
+@pytest.mark.parametrize("cols", [1, 17, 64, 65, 255, 1023, 1024, 1025, 3000])
+@pytest.mark.parametrize("dtype,op", [("int32", "sum"), ("uint32", "max"), ("int32", "max"),
+                                      ("int32", "xor"), ("float32", "sum"), ("float32", "max")])
+@pytest.mark.parametrize("kind", BLOCK_SCANS)
+def test_block_scan_variants_match_oracle(kind, dtype, op, cols):
+    rows = max(2, min(200, 100_000 // cols))
+    x = wl.case(dtype, op, rows * cols, seed=cols + 3).reshape(rows, cols)
+    check_variant(x, op, True, kind)
+    check_variant(x, op, False, kind)
+
+
+@pytest.mark.parametrize("kind", BLOCK_SCANS)
+def test_block_scan_variants_rows1024_workload(kind):
+    check_variant(wl.rows1024(), "sum", True, kind)
+

@@ -1,0 +1,66 @@
+"""Parity of the three device-wide schemes (single pass, reduce-then-scan,
+scan-then-propagate) through scan_ex, against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_scan_stream_amd as ps
+import workloads as wl
+from gpu_util import DEV, bits, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TILE = 16384  # the library tile; the sizes span tiles, ragged tails and many tiles
+SCHEMES = ["single_pass", "reduce_then_scan", "scan_then_propagate"]
+COMBOS = [("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("uint32", "max"),
+          ("float32", "sum"), ("float32", "max")]
+
+
+def check(x, op, inclusive, scheme, *, offset=0, inplace=False):
+    ref = oracle.scan(x, op, inclusive)
+    if offset:
+        xd = to_dev(np.concatenate([np.zeros(offset, x.dtype), x]))[offset:]
+    else:
+        xd = to_dev(x)
+    total = torch.empty(1, dtype=xd.dtype, device=DEV)
+    out = ps.scan_ex(xd, op, inclusive, scheme, out=xd if inplace else None, total=total)
+    got, tot = to_host(out), to_host(total)
+    if str(x.dtype) == "float32" and op == "sum":
+        ok, worst, k = oracle.fp32_sum_within_tolerance(got, ref)
+        assert ok, f"{scheme}: ratio {worst:.3g} at {k}"
+    else:
+        mism = np.flatnonzero(bits(got) != bits(ref.y))
+        assert mism.size == 0, f"{scheme}: {mism.size} mismatches, first at {mism[0]}"
+        assert bits(tot)[0] == bits(np.array([ref.total], x.dtype))[0]
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 4097, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, 300_003,
+                               77 * TILE + 13])
+@pytest.mark.parametrize("dtype,op", COMBOS)
+@pytest.mark.parametrize("scheme", SCHEMES)
+@pytest.mark.parametrize("inclusive", [True, False], ids=["incl", "excl"])
+def test_scheme_matches_oracle(inclusive, scheme, dtype, op, n):
+    check(wl.case(dtype, op, n, seed=n + 5), op, inclusive, scheme)
+
+
+@pytest.mark.parametrize("scheme", SCHEMES)
+def test_scheme_unaligned_inplace(scheme):
+    x = wl.case("int32", "sum", 5 * TILE + 3, seed=9)
+    check(x, "sum", True, scheme, offset=1)
+    check(x, "sum", False, scheme, inplace=True)
+    xf = wl.case("float32", "sum", 5 * TILE + 3, seed=10)
+    check(xf, "sum", False, scheme, offset=3)
+
+
+@pytest.mark.parametrize("scheme", ["reduce_then_scan", "scan_then_propagate"])
+def test_three_phase_recursive_totals(scheme):
+    """More than TILE tiles: the tile totals are themselves scanned in three phases."""
+    n = TILE * TILE + 3 * TILE + 5
+    x = wl.int_uniform(n, 0, 16, seed=31)
+    check(x, "sum", False, scheme)
+
+
+@pytest.mark.parametrize("scheme", SCHEMES)
+def test_scheme_big_scan_workload(scheme):
+    check(wl.big_scan(), "sum", False, scheme)
