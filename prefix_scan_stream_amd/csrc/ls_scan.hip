@@ -38,14 +38,14 @@ static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanne
 // Tile-local part of the scan, shared by every tile a block processes: serial
 // scan of each run, wave scan of the run totals (exclusive result in wex), and
 // the (run, wave) totals left in LDS by lane 63, in element order.
-template <class Op>
-__device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[SCAN_CHUNKS],
-                                                typename Op::T (&wex)[SCAN_CHUNKS],
+template <class Op, int CHUNKS = SCAN_CHUNKS>
+__device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[CHUNKS],
+                                                typename Op::T (&wex)[CHUNKS],
                                                 typename Op::T* s_part, int lane, int wave)
 {
     using T = typename Op::T;
 #pragma unroll
-    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+    for (int j = 0; j < CHUNKS; ++j) {
         r[j].v[1] = Op::apply(r[j].v[0], r[j].v[1]);
         r[j].v[2] = Op::apply(r[j].v[1], r[j].v[2]);
         r[j].v[3] = Op::apply(r[j].v[2], r[j].v[3]);
@@ -61,15 +61,17 @@ __device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[SCAN_C
 #endif
 
 // One tile per block; blocks take tile ids in the order they start.
-template <class Op, bool INCLUSIVE, bool VEC>
+template <class Op, bool INCLUSIVE, bool VEC, int CHUNKS>
 __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     const typename Op::T* in, typename Op::T* out, int64_t n, int64_t num_tiles, WsHeader* hdr,
     uint64_t* status, typename Op::T* total)
 {
     using T = typename Op::T;
     using Codec = ScanCodec<Op>;
-    constexpr int PARTS = SCAN_CHUNKS * SCAN_WAVES;  // (run, wave) partial totals per tile
+    constexpr int PARTS = CHUNKS * SCAN_WAVES;  // (run, wave) partial totals per tile
+    constexpr int TILE = SCAN_BLOCK * CHUNKS * 4;
     constexpr uint32_t RUN_STRIDE = SCAN_BLOCK * 16u;
+    static_assert(PARTS <= 64, "the (run, wave) totals are scanned by one wave");
     __shared__ T s_part[PARTS + LS_SCAN_LDS_RESERVE];
     __shared__ uint32_t s_tile;
 
@@ -82,10 +84,10 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
         s_tile = take_tile_id(hdr);
     __syncthreads();
     const int64_t tile = s_tile;
-    const int64_t tbase = tile * SCAN_TILE;
+    const int64_t tbase = tile * TILE;
     const int64_t rem = n - tbase;
-    const uint32_t valid = rem < SCAN_TILE ? uint32_t(rem) : uint32_t(SCAN_TILE);
-    const bool full = valid == SCAN_TILE;
+    const uint32_t valid = rem < TILE ? uint32_t(rem) : uint32_t(TILE);
+    const bool full = valid == TILE;
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + tbase, valid * 4u);
     const uint32_t voff = uint32_t(tid) * 16u;  // run j of thread t: elements 4*(j*BLOCK + t) + 0..3
@@ -93,14 +95,14 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     // 1. load.  Elements past n (last tile only) read as 0 (the buffer range is
     // checked per 32-bit word); they sit after every valid element in scan order,
     // so no output below n depends on them.
-    Run4<T> r[SCAN_CHUNKS];
+    Run4<T> r[CHUNKS];
 #pragma unroll
-    for (int j = 0; j < SCAN_CHUNKS; ++j)
+    for (int j = 0; j < CHUNKS; ++j)
         r[j] = VEC ? load_run_x4<T>(rin, voff, j * RUN_STRIDE) : load_run_x1<T>(rin, voff, j * RUN_STRIDE);
 
     // 2. local scan: runs, wave scan of run totals, (run, wave) totals to LDS
-    T wex[SCAN_CHUNKS];
-    scan_tile_local<Op>(r, wex, s_part, lane, wave);
+    T wex[CHUNKS];
+    scan_tile_local<Op, CHUNKS>(r, wex, s_part, lane, wave);
     __syncthreads();
 
     // 3. wave 0: scan the partial totals (one per lane), publish the tile total,
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     // 4. finish and store; the thread holding element n-1 writes the total
     const int64_t last_local = (tile == num_tiles - 1) ? int64_t(valid) - 1 : -1;
 #pragma unroll
-    for (int j = 0; j < SCAN_CHUNKS; ++j) {
+    for (int j = 0; j < CHUNKS; ++j) {
         const T cp = Op::apply(s_part[j * SCAN_WAVES + wave], wex[j]);
         Run4<T> o;
         if constexpr (INCLUSIVE) {
@@ -337,6 +339,8 @@ int64_t scan_tile_elems() { return SCAN_TILE; }
 
 static int64_t num_tiles_for(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
 
+static int64_t single_pass_tiles(int64_t n) { return num_tiles_for(n); }
+
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Single pass: header + one status word per tile.  Three-phase: tile totals and
@@ -345,11 +349,13 @@ static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 // multi-level scan).
 size_t scan_workspace_bytes(int64_t n, int scheme)
 {
+    if (scheme == SCHEME_SINGLE_PASS) {
+        const int64_t sp = single_pass_tiles(n);
+        return round256(sizeof(WsHeader) + size_t(sp < 1 ? 1 : sp) * sizeof(uint64_t));
+    }
     int64_t tiles = num_tiles_for(n);
     if (tiles < 1)
         tiles = 1;
-    if (scheme == SCHEME_SINGLE_PASS)
-        return round256(sizeof(WsHeader) + size_t(tiles) * sizeof(uint64_t));
     size_t bytes = 2 * round256(size_t(tiles) * 4);
     if (tiles > SCAN_TILE)
         bytes += scan_workspace_bytes(tiles, scheme);
@@ -375,23 +381,11 @@ template <> uint32_t identity_bits<MaxI32>() { return 0x80000000u; }
 template <> uint32_t identity_bits<SumF32>() { return 0u; }
 template <> uint32_t identity_bits<MaxF32>() { return 0xff800000u; }
 
-template <class Op>
-static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive, void* total,
-                           void* ws, hipStream_t s)
+template <class Op, int CHUNKS>
+static void launch_single_pass(const void* in, void* out, int64_t n, int64_t tiles, bool inclusive,
+                               void* total, WsHeader* hdr, uint64_t* status, hipStream_t s)
 {
     using T = typename Op::T;
-    if (n == 0) {
-        if (total)
-            hipLaunchKernelGGL(store_u32_kernel, dim3(1), dim3(64), 0, s,
-                               reinterpret_cast<uint32_t*>(total), identity_bits<Op>());
-        return hipGetLastError();
-    }
-    const int64_t tiles = num_tiles_for(n);
-    hipError_t e = clear_workspace(ws, tiles, s);
-    if (e != hipSuccess)
-        return e;
-    auto* hdr = reinterpret_cast<WsHeader*>(ws);
-    auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
     const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
     const T* pin = reinterpret_cast<const T*>(in);
     T* pout = reinterpret_cast<T*>(out);
@@ -399,19 +393,38 @@ static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive,
     const dim3 grid(static_cast<uint32_t>(tiles)), block(SCAN_BLOCK);
     if (inclusive) {
         if (vec)
-            hipLaunchKernelGGL((scan_single_pass_kernel<Op, true, true>), grid, block, 0, s, pin, pout,
-                               n, tiles, hdr, status, ptot);
+            hipLaunchKernelGGL((scan_single_pass_kernel<Op, true, true, CHUNKS>), grid, block, 0, s, pin,
+                               pout, n, tiles, hdr, status, ptot);
         else
-            hipLaunchKernelGGL((scan_single_pass_kernel<Op, true, false>), grid, block, 0, s, pin,
+            hipLaunchKernelGGL((scan_single_pass_kernel<Op, true, false, CHUNKS>), grid, block, 0, s, pin,
                                pout, n, tiles, hdr, status, ptot);
     } else {
         if (vec)
-            hipLaunchKernelGGL((scan_single_pass_kernel<Op, false, true>), grid, block, 0, s, pin,
+            hipLaunchKernelGGL((scan_single_pass_kernel<Op, false, true, CHUNKS>), grid, block, 0, s, pin,
                                pout, n, tiles, hdr, status, ptot);
         else
-            hipLaunchKernelGGL((scan_single_pass_kernel<Op, false, false>), grid, block, 0, s, pin,
+            hipLaunchKernelGGL((scan_single_pass_kernel<Op, false, false, CHUNKS>), grid, block, 0, s, pin,
                                pout, n, tiles, hdr, status, ptot);
     }
+}
+
+template <class Op>
+static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive, void* total,
+                           void* ws, hipStream_t s)
+{
+    if (n == 0) {
+        if (total)
+            hipLaunchKernelGGL(store_u32_kernel, dim3(1), dim3(64), 0, s,
+                               reinterpret_cast<uint32_t*>(total), identity_bits<Op>());
+        return hipGetLastError();
+    }
+    const int64_t tiles = single_pass_tiles(n);
+    hipError_t e = clear_workspace(ws, tiles, s);
+    if (e != hipSuccess)
+        return e;
+    auto* hdr = reinterpret_cast<WsHeader*>(ws);
+    auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
+    launch_single_pass<Op, SCAN_CHUNKS>(in, out, n, tiles, inclusive, total, hdr, status, s);
     return hipGetLastError();
 }
 
