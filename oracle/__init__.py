@@ -67,6 +67,10 @@ def _bind(lib):
     lib.oracle_batched_f32_sum.restype = None
     lib.oracle_batched_f32_max.argtypes = [P, P, I64, I64, I]
     lib.oracle_batched_f32_max.restype = None
+    lib.oracle_stable_sort.argtypes = [P, P, I64, I, P, P]
+    lib.oracle_stable_sort.restype = I
+    lib.oracle_sort_order_key.argtypes = [I, U32]
+    lib.oracle_sort_order_key.restype = U32
     return lib
 
 
@@ -201,6 +205,32 @@ class Oracle:
         raise ValueError(f"oracle: op {op} is not defined for float32")
 
 
+    def sort(self, keys: np.ndarray, values: np.ndarray | None = None):
+        """Stable ascending sort of 32-bit keys in their type's order (float32: IEEE
+        total order); values, when given, follow their keys.  Returns (keys, values)."""
+        lib = self._lib
+        k = np.ascontiguousarray(keys).copy()
+        dt = _dtype_name(k)
+        n = k.shape[0]
+        ku = k.view(np.uint32)
+        tk = np.empty(max(n, 1), np.uint32)
+        v = None
+        tv = None
+        if values is not None:
+            v = np.ascontiguousarray(values).copy()
+            if v.dtype.itemsize != 4 or v.shape[0] != n:
+                raise ValueError("oracle.sort: values must be n 32-bit elements")
+            tv = np.empty(max(n, 1), np.uint32)
+        rc = lib.oracle_stable_sort(_ptr(ku), None if v is None else _ptr(v.view(np.uint32)), n,
+                                    DTYPES[dt], _ptr(tk), None if tv is None else _ptr(tv))
+        if rc:
+            raise ValueError("oracle.sort: bad dtype")
+        return k, v
+
+    def order_key(self, dtype: str, bits: int) -> int:
+        return int(self._lib.oracle_sort_order_key(DTYPES[dtype], int(bits) & 0xFFFFFFFF))
+
+
 _default = None
 
 
@@ -221,6 +251,10 @@ def compact(x: np.ndarray, cmp: str, threshold, via_scan: bool = False):
 
 def batched(x: np.ndarray, op: str = "sum", inclusive: bool = False) -> ScanResult:
     return default().batched(x, op, inclusive)
+
+
+def sort(keys: np.ndarray, values: np.ndarray | None = None):
+    return default().sort(keys, values)
 
 
 def fp32_sum_within_tolerance(got: np.ndarray, ref: ScanResult, rel: float = 1e-6,

@@ -266,3 +266,71 @@ void oracle_batched_f32_max(const float *x, float *y, int64_t rows, int64_t cols
     for (int64_t r = 0; r < rows; ++r)
         oracle_scan_f32_max(x + r * cols, y + r * cols, cols, inclusive, 0);
 }
+
+/* ---- radix-sort order and stable sort --------------------------------------
+ * The radix sort of the pages ([Scan3] 一: each round places keys by the scan of
+ * a digit predicate; [Blog2] 4.2: per-digit histograms, their prefix sums, and a
+ * reordering) orders keys by their bits once mapped to unsigned integers whose
+ * order is the key type's order:
+ *   uint32  the key itself
+ *   int32   key with the sign bit flipped (two's complement order)
+ *   float32 negative (sign set): all bits flipped; else sign bit set.  This is
+ *           the IEEE total order: -NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN.
+ * The sort is stable: equal keys keep their input order (and so do their values).
+ * The oracle sorts by that order with a plain top-down merge sort (stable because
+ * ties take the left run first).  tmp_k / tmp_v are caller scratch of n elements. */
+uint32_t oracle_sort_order_key(int dtype, uint32_t k)
+{
+    if (dtype == OR_INT32)
+        return k ^ 0x80000000u;
+    if (dtype == OR_FLOAT32)
+        return (k & 0x80000000u) ? ~k : (k | 0x80000000u);
+    return k;
+}
+
+static void merge_sort_rec(uint32_t *k, uint32_t *v, uint32_t *tk, uint32_t *tv, int64_t lo,
+                           int64_t hi, int dtype, int with_values)
+{
+    if (hi - lo < 2)
+        return;
+    int64_t mid = lo + (hi - lo) / 2;
+    merge_sort_rec(k, v, tk, tv, lo, mid, dtype, with_values);
+    merge_sort_rec(k, v, tk, tv, mid, hi, dtype, with_values);
+    int64_t i = lo, j = mid, o = lo;
+    while (i < mid || j < hi) {
+        int take_left;
+        if (i >= mid)
+            take_left = 0;
+        else if (j >= hi)
+            take_left = 1;
+        else  /* ties: left first -> stable */
+            take_left = oracle_sort_order_key(dtype, k[i]) <= oracle_sort_order_key(dtype, k[j]);
+        if (take_left) {
+            tk[o] = k[i];
+            if (with_values)
+                tv[o] = v[i];
+            ++i;
+        } else {
+            tk[o] = k[j];
+            if (with_values)
+                tv[o] = v[j];
+            ++j;
+        }
+        ++o;
+    }
+    for (int64_t t = lo; t < hi; ++t) {
+        k[t] = tk[t];
+        if (with_values)
+            v[t] = tv[t];
+    }
+}
+
+/* Sorts keys (and values, when vals != NULL) in place.  Returns 0, or -1 on a bad code. */
+int oracle_stable_sort(uint32_t *keys, uint32_t *vals, int64_t n, int dtype, uint32_t *tmp_k,
+                       uint32_t *tmp_v)
+{
+    if (dtype < OR_INT32 || dtype > OR_FLOAT32)
+        return -1;
+    merge_sort_rec(keys, vals, tmp_k, tmp_v, 0, n, dtype, vals != 0);
+    return 0;
+}

@@ -307,4 +307,73 @@ def pin_batched_rows(orc):
     assert np.allclose(r.bound, np.cumsum(xf.astype(np.float64), axis=1), rtol=1e-14)
 
 
+# ---------------------------------------------------------------- stable sort
+
+def _order_key_np(dtype, bits_u32):
+    """The sort order as unsigned integers, computed here with numpy bit operations
+    (independent of the oracle): int32 flips the sign bit; float32 flips all bits of
+    negatives and sets the sign bit of the rest (IEEE total order)."""
+    b = bits_u32.astype(np.uint32)
+    if dtype == "int32":
+        return b ^ np.uint32(0x80000000)
+    if dtype == "float32":
+        neg = (b & np.uint32(0x80000000)) != 0
+        return np.where(neg, ~b, b | np.uint32(0x80000000)).astype(np.uint32)
+    return b
+
+
+def pin_sort_matches_numpy_stable_argsort(orc):
+    rng = np.random.default_rng(17)
+    for dtype in ("int32", "uint32", "float32"):
+        for n in (1, 2, 7, 100, 5000):
+            if dtype == "float32":
+                k = (rng.standard_normal(n) * 10).round().astype(np.float32)
+                k[::5] = -0.0
+            elif dtype == "int32":
+                k = rng.integers(-50, 50, n).astype(np.int32)
+            else:
+                k = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+                k[::3] = 7
+            v = np.arange(n, dtype=np.uint32)
+            sk, sv = orc.sort(k, v)
+            order = np.argsort(_order_key_np(dtype, k.view(np.uint32)), kind="stable")
+            assert _bits(sk) == _bits(k[order])
+            assert sv.tolist() == order.tolist()
+            # keys only: the same keys
+            assert _bits(orc.sort(k)[0]) == _bits(k[order])
+    ints = rng.integers(-(1 << 31), 1 << 31, 3000, dtype=np.int64).astype(np.int32)
+    assert np.array_equal(orc.sort(ints)[0], np.sort(ints))
+    uints = ints.view(np.uint32)
+    assert np.array_equal(orc.sort(uints)[0], np.sort(uints))
+
+
+def pin_sort_brute_force_and_invariants(orc):
+    rng = np.random.default_rng(19)
+    for n in range(1, 9):
+        for _ in range(20):
+            k = rng.integers(-3, 3, n).astype(np.int32)
+            v = np.arange(n, dtype=np.uint32)
+            sk, sv = orc.sort(k, v)
+            # insertion sort, stable by construction
+            pairs = list(zip(k.tolist(), v.tolist()))
+            for i in range(1, len(pairs)):
+                j = i
+                while j > 0 and pairs[j - 1][0] > pairs[j][0]:
+                    pairs[j - 1], pairs[j] = pairs[j], pairs[j - 1]
+                    j -= 1
+            assert sk.tolist() == [p[0] for p in pairs]
+            assert sv.tolist() == [p[1] for p in pairs]
+    k = rng.integers(0, 20, 10000).astype(np.uint32)
+    v = np.arange(10000, dtype=np.uint32)
+    sk, sv = orc.sort(k, v)
+    assert np.all(sk[1:] >= sk[:-1])                           # ordered
+    assert np.array_equal(np.sort(sv), v)                       # a permutation
+    assert np.array_equal(k[sv], sk)                            # values follow keys
+    same = sk[1:] == sk[:-1]
+    assert np.all(sv[1:][same] > sv[:-1][same])                 # stable
+    f = np.array([np.nan, 1.0, -np.nan, -0.0, 0.0, -np.inf, np.inf, -1.0], np.float32)
+    want = [-np.nan, -np.inf, -1.0, -0.0, 0.0, 1.0, np.inf, np.nan]
+    assert _bits(orc.sort(f)[0]) == _bits(np.array(want, np.float32))
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,6 +39,12 @@ MUTANTS = [
      "oracle_scan_u32(x + r, y + r * cols,"),
     ("batched_f32_carry", "oracle_scan_f32_sum(x + r * cols, y + r * cols,",
      "oracle_scan_f32_sum(x, y + r * cols,"),
+    ("sort_unstable_ties", "take_left = oracle_sort_order_key(dtype, k[i]) <= oracle_sort_order_key(dtype, k[j]);",
+     "take_left = oracle_sort_order_key(dtype, k[i]) < oracle_sort_order_key(dtype, k[j]);"),
+    ("sort_int32_unsigned", "        return k ^ 0x80000000u;\n    if (dtype == OR_FLOAT32)",
+     "        return k;\n    if (dtype == OR_FLOAT32)"),
+    ("sort_float_negatives", "return (k & 0x80000000u) ? ~k : (k | 0x80000000u);",
+     "return (k & 0x80000000u) ? (k ^ 0x80000000u) : (k | 0x80000000u);"),
 ]
 
 
