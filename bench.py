@@ -36,9 +36,8 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
 ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
-            "blockscans")
-DEFAULT_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
-                "blockscans")
+            "blockscans", "sort")
+DEFAULT_LEGS = ALL_LEGS
 
 
 def log(msg):
@@ -242,6 +241,22 @@ def main():
             bw_leg(f"rows_2e16x1024_i32_excl_{kind}", xs,
                    lambda a, b, k=kind: ps.batched_row_scan_ex(a, "sum", True, k, out=b), n, 8 * n)
         del xs
+    if "sort" in legs:
+        # stable LSD radix sort (4 passes of 8 bits) of 2^24 uint32 keys, with and
+        # without 32-bit values; per pass: histogram read, scatter read + write
+        n = 1 << 24
+        keys = to_dev(wl.u32_bits(n, seed=99))
+        vals = torch.arange(n, dtype=torch.int32, device=dev)
+        ok_, ov_ = torch.empty_like(keys), torch.empty_like(vals)
+        for name, v, per_pass in (("sort_u32_pairs_2e24", vals, 20), ("sort_u32_keys_2e24", None, 12)):
+            ms = timer.run(lambda i, v=v: ps.radix_sort(keys, v, out_keys=ok_,
+                                                        out_values=ov_ if v is not None else None), K, W)
+            moved = 4 * per_pass * n
+            result_legs[name] = {"us": round(ms * 1e3, 1), "gkeys_s": round(n / ms / 1e6, 2),
+                                 "moved_gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                                 "bytes_moved_per_key": 4 * per_pass}
+            log(f"{name}: {ms * 1e3:.1f} us, {n / ms / 1e6:.2f} Gkeys/s")
+        del keys, vals, ok_, ov_
     if "copy" in legs:
         n = wl.SIZES["big_scan"]
         a = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)

@@ -190,6 +190,33 @@ ls_status batched_row_scan(const void *in, void *out, int64_t rows, int64_t cols
 ls_status batched_row_scan_ex(const void *in, void *out, int64_t rows, int64_t cols, ls_dtype t,
                               ls_op op, int exclusive, ls_block_scan block_scan, void *stream);
 
+/* Workspace size for radix_sort (with_values: nonzero when values are sorted
+ * along).  Errors: LS_ERR_INVALID_ARG for n < 0, n >= 2^32, bytes == NULL or an
+ * unknown dtype. */
+ls_status ls_radix_sort_workspace_bytes(int64_t n, ls_dtype t, int with_values, size_t *bytes);
+
+/* Stable ascending radix sort of 32-bit keys, optionally carrying 32-bit values.
+ * The pages' scan application ([Scan3] 一: each pass places keys by the scan of
+ * a digit predicate, one group offset by the size of the others; [Blog2] 4.2:
+ * per-digit histograms, their prefix sums, a reordering).
+ *   keys_in, keys_out      n elements of type t.  keys_out == keys_in (in place)
+ *                          is allowed; other overlap is LS_ERR_INVALID_ARG.
+ *   values_in, values_out  both NULL (keys only) or both non-NULL: n 32-bit
+ *                          values moved with their keys; values_out ==
+ *                          values_in allowed.  One NULL and one not is
+ *                          LS_ERR_INVALID_ARG.
+ *   n                      0 <= n < 2^32.
+ *   t                      key order: int32 signed, uint32 unsigned, float32
+ *                          IEEE total order (-NaN < -inf < ... < -0 < +0 < ...
+ *                          < +inf < +NaN, by bit pattern within NaNs).
+ *   ws                     >= ls_radix_sort_workspace_bytes(n, t, values != NULL)
+ *                          bytes, 16-byte aligned, overlapping no other buffer.
+ * Equal keys keep their input order (the sort is stable), so the result,
+ * values included, is unique.  Four passes of 8-bit digits; each reads the keys
+ * twice and writes them once. */
+ls_status radix_sort(const void *keys_in, void *keys_out, const void *values_in, void *values_out,
+                     int64_t n, ls_dtype t, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

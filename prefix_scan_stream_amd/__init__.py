@@ -22,7 +22,7 @@ __all__ = [
     "LibscanError", "library_path", "load_library", "ls_abi_version", "ls_status_string",
     "ls_scan_workspace_bytes", "ls_compact_workspace_bytes", "scan_inclusive", "scan_exclusive",
     "compact_if", "batched_row_scan", "workspace_for", "scan_ex", "ls_scan_ex_workspace_bytes",
-    "batched_row_scan_ex",
+    "batched_row_scan_ex", "radix_sort", "ls_radix_sort_workspace_bytes",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +84,10 @@ def load_library():
         lib.scan_ex.restype = I
         lib.batched_row_scan_ex.argtypes = [P, P, I64, I64, I, I, I, I, P]
         lib.batched_row_scan_ex.restype = I
+        lib.ls_radix_sort_workspace_bytes.argtypes = [I64, I, I, ctypes.POINTER(SZ)]
+        lib.ls_radix_sort_workspace_bytes.restype = I
+        lib.radix_sort.argtypes = [P, P, P, P, I64, I, P, SZ, P]
+        lib.radix_sort.restype = I
         lib.compact_if.argtypes = [P, P, P, I64, I, I, U32, P, SZ, P]
         lib.compact_if.restype = I
         lib.batched_row_scan.argtypes = [P, P, I64, I64, I, I, I, P]
@@ -292,3 +296,37 @@ def batched_row_scan_ex(x: torch.Tensor, op: str = "sum", exclusive: bool = True
                                  1 if exclusive else 0, BLOCK_SCAN_CODES[block_scan], sh)
     _check(st, "batched_row_scan_ex")
     return out
+
+
+def ls_radix_sort_workspace_bytes(n: int, dtype: str, with_values: bool) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ls_radix_sort_workspace_bytes(n, DTYPE_CODES[dtype], 1 if with_values else 0,
+                                                        ctypes.byref(out)),
+           "ls_radix_sort_workspace_bytes")
+    return out.value
+
+
+def radix_sort(keys: torch.Tensor, values: torch.Tensor | None = None,
+               out_keys: torch.Tensor | None = None, out_values: torch.Tensor | None = None):
+    """Stable ascending sort of a flat 32-bit key tensor (int32 / uint32 / float32 in
+    IEEE total order), with optional 32-bit values.  Returns (keys, values or None)."""
+    lib = load_library()
+    _require_gpu(keys, values, out_keys, out_values)
+    if not keys.is_contiguous() or (values is not None and not values.is_contiguous()):
+        raise ValueError("libscan: keys and values must be contiguous")
+    dt = _dtype_of(keys)
+    n = keys.numel()
+    if values is not None and (values.numel() != n or values.element_size() != 4):
+        raise ValueError("libscan: values must hold n 32-bit elements")
+    if out_keys is None:
+        out_keys = torch.empty_like(keys)
+    if values is not None and out_values is None:
+        out_values = torch.empty_like(values)
+    stream, sh = _stream_handle(keys.device)
+    need = ls_radix_sort_workspace_bytes(n, dt, values is not None)
+    ws = workspace_for(keys.device, stream, need)
+    st = lib.radix_sort(_ptr(keys), _ptr(out_keys), _ptr(values), _ptr(out_values), n, DTYPE_CODES[dt],
+                        _ptr(ws), ws.numel(), sh)
+    _check(st, "radix_sort")
+    return out_keys, (out_values if values is not None else None)
+

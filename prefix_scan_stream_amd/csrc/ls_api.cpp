@@ -191,4 +191,50 @@ ls_status batched_row_scan_ex(const void* in, void* out, int64_t rows, int64_t c
     return batched_common(in, out, rows, cols, t, op, exclusive, block_scan, stream);
 }
 
+ls_status ls_radix_sort_workspace_bytes(int64_t n, ls_dtype t, int with_values, size_t* bytes)
+{
+    if (bytes == nullptr || n < 0 || n > int64_t(UINT32_MAX) || !valid_dtype(t))
+        return LS_ERR_INVALID_ARG;
+    *bytes = ls::sort_workspace_bytes(n, with_values != 0);
+    return LS_OK;
+}
+
+ls_status radix_sort(const void* keys_in, void* keys_out, const void* values_in, void* values_out,
+                     int64_t n, ls_dtype t, void* ws, size_t ws_bytes, void* stream)
+{
+    if (n < 0 || n > int64_t(UINT32_MAX) || !valid_dtype(t))
+        return LS_ERR_INVALID_ARG;
+    if ((values_in == nullptr) != (values_out == nullptr))
+        return LS_ERR_INVALID_ARG;
+    const bool vals = values_in != nullptr;
+    const size_t bytes = size_t(n) * 4;
+    if (n > 0) {
+        if (keys_in == nullptr || keys_out == nullptr || !aligned(keys_in, 4) || !aligned(keys_out, 4))
+            return LS_ERR_INVALID_ARG;
+        if (keys_in != keys_out && overlaps(keys_in, bytes, keys_out, bytes))
+            return LS_ERR_INVALID_ARG;
+        if (vals) {
+            if (!aligned(values_in, 4) || !aligned(values_out, 4))
+                return LS_ERR_INVALID_ARG;
+            if (values_in != values_out && overlaps(values_in, bytes, values_out, bytes))
+                return LS_ERR_INVALID_ARG;
+            const void* ks[2] = {keys_in, keys_out};
+            const void* vs[2] = {values_in, values_out};
+            for (const void* a : ks)
+                for (const void* b : vs)
+                    if (overlaps(a, bytes, b, bytes))
+                        return LS_ERR_INVALID_ARG;
+        }
+    }
+    const size_t need = ls::sort_workspace_bytes(n, vals);
+    ls_status st = check_ws(ws, ws_bytes, need);
+    if (st != LS_OK)
+        return st;
+    if (!aligned(ws, 16) || overlaps(ws, need, keys_in, bytes) || overlaps(ws, need, keys_out, bytes) ||
+        (vals && (overlaps(ws, need, values_in, bytes) || overlaps(ws, need, values_out, bytes))))
+        return LS_ERR_INVALID_ARG;
+    return from_hip(ls::launch_sort(keys_in, keys_out, values_in, values_out, n, int(t), ws,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

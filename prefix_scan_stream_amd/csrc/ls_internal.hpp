@@ -33,4 +33,9 @@ hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, 
 hipError_t launch_batched(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int op,
                           bool exclusive, int kind, hipStream_t stream);
 
+// ---- radix sort (ls_sort.hip)
+size_t sort_workspace_bytes(int64_t n, bool with_values);
+hipError_t launch_sort(const void* keys_in, void* keys_out, const void* vals_in, void* vals_out,
+                       int64_t n, int dtype, void* ws, hipStream_t stream);
+
 }  // namespace ls

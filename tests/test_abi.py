@@ -138,6 +138,33 @@ def test_extended_entry_points_validation(lib):
     assert lib.batched_row_scan_ex(None, None, 0, 5, INT32, SUM, 1, 2, None) == ps.LS_OK
 
 
+def test_radix_sort_validation(lib):
+    A_V1, A_V2 = 0x7F0040000000, 0x7F0050000000
+    sz = ctypes.c_size_t(0)
+    assert lib.ls_radix_sort_workspace_bytes(1 << 20, UINT32, 1, ctypes.byref(sz)) == 0
+    with_v = sz.value
+    assert lib.ls_radix_sort_workspace_bytes(1 << 20, UINT32, 0, ctypes.byref(sz)) == 0
+    assert with_v > sz.value > 0
+    assert lib.ls_radix_sort_workspace_bytes(-1, UINT32, 0, ctypes.byref(sz)) == INV
+    assert lib.ls_radix_sort_workspace_bytes(1 << 32, UINT32, 0, ctypes.byref(sz)) == INV
+    assert lib.ls_radix_sort_workspace_bytes(10, 5, 0, ctypes.byref(sz)) == INV
+
+    def rs(ki=A_IN, ko=A_OUT, vi=None, vo=None, n=100, t=UINT32, ws=A_WS, wsb=BIG_WS):
+        return lib.radix_sort(ki, ko, vi, vo, n, t, ws, wsb, None)
+
+    assert rs(n=-1) == INV
+    assert rs(n=1 << 32) == INV
+    assert rs(t=7) == INV
+    assert rs(vi=A_V1) == INV            # values in without values out
+    assert rs(vo=A_V2) == INV
+    assert rs(ki=None) == INV
+    assert rs(ko=A_IN + 8) == INV        # partial overlap of keys
+    assert rs(vi=A_V1, vo=A_IN) == INV   # values overlap keys
+    assert rs(ws=None) == WS
+    assert rs(n=1 << 20, wsb=4096) == WS
+    assert rs(ws=A_WS + 4) == INV        # workspace alignment
+
+
 def test_compact_validation(lib):
     def call(inp=A_IN, out=A_OUT, count=A_TOT, n=10, t=INT32, cmp=0, ws=A_WS, wsb=BIG_WS):
         return lib.compact_if(inp, out, count, n, t, cmp, 5, ws, wsb, None)
