@@ -8,14 +8,16 @@
 // them, and a reordering (lpnh.cn parallel scan overview, section 4.2).
 //
 // Here: four passes of 8-bit digits, least significant first.  Each pass is
-//   1. histogram: every wave owns a tile of RS_TILE consecutive keys and counts
-//      its digits in LDS; counts go to hist[digit * tiles + tile] (digit-major);
+//   1. histogram: every block counts the digits of a tile of RS_TILE consecutive
+//      keys in LDS; counts go to hist[digit * tiles + tile] (digit-major);
 //   2. the library's own single-pass exclusive scan over hist -- after it,
 //      hist[d * tiles + t] is where tile t's first key of digit d goes;
-//   3. scatter: each wave walks its tile in input order, 64 keys at a time, and
-//      ranks each key among the equal digits of that group with 8 ballots (one
-//      per digit bit); per-digit cursors in LDS carry the ranks across groups.
-//      Equal keys keep their order: the pass is stable, so the sort is.
+//   3. scatter: each wave walks its quarter of the tile in input order, 64 keys
+//      at a time, and ranks each key among the equal digits of that group with
+//      8 ballots (one per digit bit); per-digit cursors in LDS carry the ranks
+//      across groups.  The block then groups its keys by digit in LDS and writes
+//      each digit's run to consecutive output addresses.  Equal keys keep their
+//      order: the pass is stable, so the sort is.
 // Keys are compared in their type's order through an order-preserving map to
 // unsigned integers (int32: sign bit flipped; float32: IEEE total order).
 #include "ls_device.hpp"
@@ -23,13 +25,15 @@
 
 namespace ls {
 
-constexpr int RS_BLOCK = 256;  // four independent waves
+constexpr int RS_BLOCK = 256;
 constexpr int RS_WAVES = RS_BLOCK / 64;
-constexpr int RS_ITEMS = 16;   // keys per lane per tile
-constexpr int RS_TILE = 64 * RS_ITEMS;  // 1024 keys per wave tile
+constexpr int RS_ITEMS = 16;                   // keys per lane
+constexpr int RS_WTILE = 64 * RS_ITEMS;        // 1024 keys per wave
+constexpr int RS_TILE = RS_WAVES * RS_WTILE;   // 4096 keys per block tile
 constexpr int RS_BITS = 8;
 constexpr int RS_DIGITS = 1 << RS_BITS;
 constexpr int RS_PASSES = 32 / RS_BITS;
+static_assert(RS_DIGITS == RS_BLOCK, "one thread per digit in the block-wide steps");
 
 template <int DT>
 __device__ __forceinline__ uint32_t order_key(uint32_t k)
@@ -42,93 +46,156 @@ __device__ __forceinline__ uint32_t order_key(uint32_t k)
         return k;
 }
 
-// Key i of lane l in wave tile t: element t*RS_TILE + i*64 + l, so each group of
-// 64 keys is one coalesced 256-byte load and groups come in input order.
+template <int DT>
+__device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift)
+{
+    return (order_key<DT>(k) >> shift) & (RS_DIGITS - 1);
+}
+
+// Block tile t covers keys t*RS_TILE .. +RS_TILE-1; wave w of it the 1024 keys from
+// w*RS_WTILE, key i of lane l at w*RS_WTILE + i*64 + l (a coalesced 256-byte load
+// per group of 64, groups in input order).
 template <int DT>
 __global__ __launch_bounds__(RS_BLOCK) void rs_hist_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                            int shift, uint32_t* __restrict__ hist,
                                                            int64_t tiles)
 {
-    __shared__ uint32_t cnt[RS_WAVES][RS_DIGITS];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t tile = int64_t(blockIdx.x) * RS_WAVES + wave;
-    if (tile >= tiles)
-        return;  // waves are independent: no block barrier below
-#pragma unroll
-    for (int q = 0; q < RS_DIGITS / 64; ++q)
-        cnt[wave][lane * (RS_DIGITS / 64) + q] = 0;
-    const int64_t base = tile * RS_TILE;
+    __shared__ uint32_t cnt[RS_DIGITS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t tile = blockIdx.x;
+    cnt[tid] = 0;
+    const int64_t base = tile * RS_TILE + int64_t(wave) * RS_WTILE;
     const int64_t rem = n - base;
-    const uint32_t valid = rem < RS_TILE ? uint32_t(rem) : uint32_t(RS_TILE);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(keys + base, valid * 4u);
+    const uint32_t valid = rem <= 0 ? 0u : (rem < RS_WTILE ? uint32_t(rem) : uint32_t(RS_WTILE));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(keys + (rem <= 0 ? 0 : base), valid * 4u);
     uint32_t k[RS_ITEMS];
 #pragma unroll
     for (int i = 0; i < RS_ITEMS; ++i)
         k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, uint32_t(i * 64 + lane) * 4u, 0, CACHE_NT);
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < RS_ITEMS; ++i) {
         if (uint32_t(i * 64 + lane) < valid)
-            atomicAdd(&cnt[wave][(order_key<DT>(k[i]) >> shift) & (RS_DIGITS - 1)], 1u);
+            atomicAdd(&cnt[digit_of<DT>(k[i], shift)], 1u);
     }
-#pragma unroll
-    for (int q = 0; q < RS_DIGITS / 64; ++q) {
-        const int d = lane * (RS_DIGITS / 64) + q;
-        hist[int64_t(d) * tiles + tile] = cnt[wave][d];
-    }
+    __syncthreads();
+    hist[int64_t(tid) * tiles + tile] = cnt[tid];
 }
 
+// Stable scatter of one block tile:
+//   1. each wave ranks its keys among equal digits in input order (8 ballots per
+//      group of 64, a per-wave digit cursor in LDS) and ends with its digit counts;
+//   2. one thread per digit: the block's digit runs (exclusive scan of the
+//      per-digit totals over the block), each wave's offset inside its digit's
+//      run, and the run's place in the output (the scanned histogram);
+//   3. keys (and values) are staged in LDS grouped by digit, in input order
+//      within a digit;
+//   4. the staged tile is written out: consecutive positions of one digit go to
+//      consecutive addresses, so runs of a digit are written together.
 template <int DT, bool VALS>
 __global__ __launch_bounds__(RS_BLOCK) void rs_scatter_kernel(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ offs, int64_t tiles)
 {
-    __shared__ uint32_t pos[RS_WAVES][RS_DIGITS];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t tile = int64_t(blockIdx.x) * RS_WAVES + wave;
-    if (tile >= tiles)
-        return;
+    __shared__ uint32_t s_keys[RS_TILE];
+    __shared__ uint32_t s_vals[VALS ? RS_TILE : 1];
+    __shared__ uint32_t wcnt[RS_WAVES][RS_DIGITS];   // per-wave digit counts, then offsets
+    __shared__ uint32_t run_start[RS_DIGITS];        // where a digit's run starts in the tile
+    __shared__ uint32_t run_dest[RS_DIGITS];         // where it goes in the output
+    __shared__ uint32_t s_wtot[RS_WAVES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t tile = blockIdx.x;
+
 #pragma unroll
-    for (int q = 0; q < RS_DIGITS / 64; ++q) {
-        const int d = lane * (RS_DIGITS / 64) + q;
-        pos[wave][d] = offs[int64_t(d) * tiles + tile];
-    }
-    const int64_t base = tile * RS_TILE;
+    for (int w = 0; w < RS_WAVES; ++w)
+        wcnt[w][tid] = 0;
+    const int64_t tbase = tile * RS_TILE;
+    const int64_t trem = n - tbase;
+    const uint32_t tvalid = trem < RS_TILE ? uint32_t(trem) : uint32_t(RS_TILE);
+    const int64_t base = tbase + int64_t(wave) * RS_WTILE;
     const int64_t rem = n - base;
-    const uint32_t valid = rem < RS_TILE ? uint32_t(rem) : uint32_t(RS_TILE);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin + base, valid * 4u);
-    uint32_t k[RS_ITEMS], v[RS_ITEMS];
+    const uint32_t valid = rem <= 0 ? 0u : (rem < RS_WTILE ? uint32_t(rem) : uint32_t(RS_WTILE));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin + (rem <= 0 ? 0 : base), valid * 4u);
+    uint32_t k[RS_ITEMS], v[RS_ITEMS], rank[RS_ITEMS];
 #pragma unroll
     for (int i = 0; i < RS_ITEMS; ++i)
         k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, uint32_t(i * 64 + lane) * 4u, 0, CACHE_NT);
     if constexpr (VALS) {
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vin + base, valid * 4u);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vin + (rem <= 0 ? 0 : base), valid * 4u);
 #pragma unroll
         for (int i = 0; i < RS_ITEMS; ++i)
             v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, uint32_t(i * 64 + lane) * 4u, 0, CACHE_NT);
     }
-    const uint64_t below = (uint64_t(1) << lane) - 1;  // lanes before this one
+    const uint32_t d_me = tid;  // the digit this thread handles in the block-wide steps
+    run_dest[d_me] = offs[int64_t(d_me) * tiles + tile];
+    __syncthreads();
+
+    // 1. rank inside the wave tile
+    const uint64_t below = (uint64_t(1) << lane) - 1;
 #pragma unroll
     for (int i = 0; i < RS_ITEMS; ++i) {
         const bool live = uint32_t(i * 64 + lane) < valid;
-        const uint32_t d = (order_key<DT>(k[i]) >> shift) & (RS_DIGITS - 1);
-        // lanes of this group holding the same digit
+        const uint32_t d = digit_of<DT>(k[i], shift);
         uint64_t peers = __ballot(live);
 #pragma unroll
         for (int b = 0; b < RS_BITS; ++b) {
             const uint64_t ones = __ballot((d >> b) & 1u);
             peers &= ((d >> b) & 1u) ? ones : ~ones;
         }
-        if (live) {
-            const uint32_t rank = __builtin_popcountll(peers & below);
-            const uint32_t p = pos[wave][d] + rank;
-            kout[p] = k[i];
+        const uint32_t in_group = __builtin_popcountll(peers & below);
+        const uint32_t before = live ? wcnt[wave][d] : 0u;
+        rank[i] = before + in_group;
+        if (live && in_group == 0)
+            wcnt[wave][d] = before + uint32_t(__builtin_popcountll(peers));
+    }
+    __syncthreads();
+
+    // 2. per digit: offsets of the waves inside the digit's run, the run's start in
+    // the tile (block-wide exclusive scan of the digit totals), its output place
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) {
+        const uint32_t c = wcnt[w][d_me];
+        wcnt[w][d_me] = tot;
+        tot += c;
+    }
+    const uint32_t inc = wave_inclusive_scan<SumU32>(tot);
+    if (lane == 63)
+        s_wtot[wave] = inc;
+    __syncthreads();
+    uint32_t wpre = 0;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w)
+        wpre += (w < wave) ? s_wtot[w] : 0u;
+    run_start[d_me] = wpre + inc - tot;
+    __syncthreads();
+
+    // 3. stage grouped by digit
+#pragma unroll
+    for (int i = 0; i < RS_ITEMS; ++i) {
+        if (uint32_t(i * 64 + lane) < valid) {
+            const uint32_t d = digit_of<DT>(k[i], shift);
+            const uint32_t q = run_start[d] + wcnt[wave][d] + rank[i];
+            s_keys[q] = k[i];
             if constexpr (VALS)
-                vout[p] = v[i];
-            if (rank == 0)  // the first lane of the group advances the digit's cursor
-                pos[wave][d] += uint32_t(__builtin_popcountll(peers));
+                s_vals[q] = v[i];
         }
+    }
+    __syncthreads();
+
+    // 4. write the digit runs
+    for (uint32_t q = tid; q < tvalid; q += RS_BLOCK) {
+        const uint32_t key = s_keys[q];
+        const uint32_t d = digit_of<DT>(key, shift);
+        const uint32_t dst = run_dest[d] + (q - run_start[d]);
+        kout[dst] = key;
+        if constexpr (VALS)
+            vout[dst] = s_vals[q];
     }
 }
 
@@ -167,7 +234,7 @@ static hipError_t run_sort(const uint32_t* kin, uint32_t* kout, const uint32_t* 
     uint32_t* hist = reinterpret_cast<uint32_t*>(p);
     p += rs_round(size_t(m) * 4);
     void* scan_ws = p;
-    const dim3 grid(static_cast<uint32_t>((tiles + RS_WAVES - 1) / RS_WAVES)), block(RS_BLOCK);
+    const dim3 grid(static_cast<uint32_t>(tiles)), block(RS_BLOCK);
     const uint32_t* sk = kin;
     const uint32_t* sv = vin;
     for (int pass = 0; pass < RS_PASSES; ++pass) {
