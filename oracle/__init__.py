@@ -71,6 +71,12 @@ def _bind(lib):
     lib.oracle_stable_sort.restype = I
     lib.oracle_sort_order_key.argtypes = [I, U32]
     lib.oracle_sort_order_key.restype = U32
+    lib.oracle_compact_flags.argtypes = [P, P, P, I64]
+    lib.oracle_compact_flags.restype = I64
+    lib.oracle_indices_flags.argtypes = [P, P, I64]
+    lib.oracle_indices_flags.restype = I64
+    lib.oracle_indices_if.argtypes = [P, P, I64, I, I, U32]
+    lib.oracle_indices_if.restype = I64
     return lib
 
 
@@ -227,6 +233,33 @@ class Oracle:
             raise ValueError("oracle.sort: bad dtype")
         return k, v
 
+    def compact_flags(self, x: np.ndarray, flags: np.ndarray):
+        """Elements of x (any 32-bit type) whose byte flag is nonzero, in order; count."""
+        x = np.ascontiguousarray(x)
+        f = np.ascontiguousarray(flags, dtype=np.uint8)
+        n = x.shape[0]
+        out = np.zeros(n + 1, np.uint32)
+        c = self._lib.oracle_compact_flags(_ptr(x.view(np.uint32)), _ptr(f), _ptr(out), n)
+        return out[:c].view(x.dtype).copy(), int(c)
+
+    def indices(self, flags: np.ndarray = None, x: np.ndarray = None, cmp: str = None,
+                threshold=None):
+        """Positions i (uint32) with flags[i] != 0, or with (x[i] CMP threshold)."""
+        out_n = (flags if flags is not None else x).shape[0]
+        out = np.zeros(out_n + 1, np.uint32)
+        if flags is not None:
+            f = np.ascontiguousarray(flags, dtype=np.uint8)
+            c = self._lib.oracle_indices_flags(_ptr(f), _ptr(out), out_n)
+        else:
+            x = np.ascontiguousarray(x)
+            dt = _dtype_name(x)
+            thr = np.array([threshold], dtype=x.dtype).view(np.uint32)[0]
+            c = self._lib.oracle_indices_if(_ptr(x.view(np.uint32)), _ptr(out), out_n, DTYPES[dt],
+                                            CMPS[cmp], int(thr))
+        if c < 0:
+            raise ValueError("oracle: bad index-selection arguments")
+        return out[:c].copy(), int(c)
+
     def order_key(self, dtype: str, bits: int) -> int:
         return int(self._lib.oracle_sort_order_key(DTYPES[dtype], int(bits) & 0xFFFFFFFF))
 
@@ -255,6 +288,14 @@ def batched(x: np.ndarray, op: str = "sum", inclusive: bool = False) -> ScanResu
 
 def sort(keys: np.ndarray, values: np.ndarray | None = None):
     return default().sort(keys, values)
+
+
+def compact_flags(x: np.ndarray, flags: np.ndarray):
+    return default().compact_flags(x, flags)
+
+
+def indices(flags=None, x=None, cmp=None, threshold=None):
+    return default().indices(flags, x, cmp, threshold)
 
 
 def fp32_sum_within_tolerance(got: np.ndarray, ref: ScanResult, rel: float = 1e-6,

@@ -334,3 +334,43 @@ int oracle_stable_sort(uint32_t *keys, uint32_t *vals, int64_t n, int dtype, uin
     merge_sort_rec(keys, vals, tmp_k, tmp_v, 0, n, dtype, vals != 0);
     return 0;
 }
+
+/* ---- compaction by a flag array, and index selection --------------------------
+ * [SIMT3] 4.1-4.2: the input comes with a validity mask; every element whose flag
+ * is set is copied to the output front, in order, and the count is reported.
+ * Index selection keeps the positions i instead of the values -- the output index
+ * of the compaction's scatter step read the other way round ([Scan3] 一).
+ * flags: one byte per element, nonzero = keep.  out holds n elements.
+ * Return the count (or -1 on an unknown code). */
+int64_t oracle_compact_flags(const uint32_t *x, const uint8_t *flags, uint32_t *out, int64_t n)
+{
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (flags[i] != 0)
+            out[c++] = x[i];
+    }
+    return c;
+}
+
+int64_t oracle_indices_flags(const uint8_t *flags, uint32_t *out, int64_t n)
+{
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (flags[i] != 0)
+            out[c++] = (uint32_t)i;
+    }
+    return c;
+}
+
+int64_t oracle_indices_if(const uint32_t *x, uint32_t *out, int64_t n, int dtype, int cmp,
+                          uint32_t thr_bits)
+{
+    if (dtype < OR_INT32 || dtype > OR_FLOAT32 || cmp < 0 || cmp > 5)
+        return -1;
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (pred_holds(dtype, cmp, x[i], thr_bits))
+            out[c++] = (uint32_t)i;
+    }
+    return c;
+}

@@ -307,6 +307,37 @@ def pin_batched_rows(orc):
     assert np.allclose(r.bound, np.cumsum(xf.astype(np.float64), axis=1), rtol=1e-14)
 
 
+# ---------------------------------------------------------------- flags / indices
+
+def pin_flag_compaction_and_indices(orc):
+    g = load_golden("worked_example.txt")
+    x = np.array(g["x"], np.int32)
+    flags = np.array(g["flags"], np.uint8)
+    out, c = orc.compact_flags(x, flags)
+    assert out.tolist() == g["compacted"] and c == g["count"][0]
+    idx, ci = orc.indices(flags=flags)
+    # the kept positions, read off the page's flags by numpy, and their scan values
+    assert idx.tolist() == np.flatnonzero(flags).tolist() and ci == c
+    excl = orc.scan(flags.astype(np.int32), "sum", False).y
+    assert excl[idx].tolist() == list(range(c))
+    idx2, _ = orc.indices(x=x, cmp="gt", threshold=2)
+    assert idx2.tolist() == idx.tolist()
+    rng = np.random.default_rng(23)
+    for n in (1, 10, 1000, 50_000):
+        f = (rng.random(n) < 0.3).astype(np.uint8) * rng.integers(1, 256, n).astype(np.uint8)
+        xv = rng.integers(-(1 << 31), 1 << 31, n, dtype=np.int64).astype(np.int32)
+        out, c = orc.compact_flags(xv, f)
+        assert np.array_equal(out, xv[f != 0]) and c == int(np.count_nonzero(f))
+        assert np.array_equal(orc.indices(flags=f)[0], np.flatnonzero(f).astype(np.uint32))
+        for cmp, fn in (("lt", np.less), ("ge", np.greater_equal), ("eq", np.equal)):
+            want = np.flatnonzero(fn(xv, 17)).astype(np.uint32)
+            assert np.array_equal(orc.indices(x=xv, cmp=cmp, threshold=17)[0], want)
+        xf = xv.view(np.float32)
+        out, c = orc.compact_flags(xf, f)
+        assert _bits(out) == _bits(xf[f != 0])      # payload bits copied, whatever they are
+    assert orc.indices(flags=np.zeros(0, np.uint8))[1] == 0
+
+
 # ---------------------------------------------------------------- stable sort
 
 def _order_key_np(dtype, bits_u32):

@@ -39,6 +39,10 @@ MUTANTS = [
      "oracle_scan_u32(x + r, y + r * cols,"),
     ("batched_f32_carry", "oracle_scan_f32_sum(x + r * cols, y + r * cols,",
      "oracle_scan_f32_sum(x, y + r * cols,"),
+    ("flags_keep_zero", "        if (flags[i] != 0)\n            out[c++] = x[i];",
+     "        if (flags[i] == 0)\n            out[c++] = x[i];"),
+    ("indices_off_by_one", "            out[c++] = (uint32_t)i;\n    }\n    return c;\n}\n\nint64_t oracle_indices_if",
+     "            out[c++] = (uint32_t)(i + 1);\n    }\n    return c;\n}\n\nint64_t oracle_indices_if"),
     ("sort_unstable_ties", "take_left = oracle_sort_order_key(dtype, k[i]) <= oracle_sort_order_key(dtype, k[j]);",
      "take_left = oracle_sort_order_key(dtype, k[i]) < oracle_sort_order_key(dtype, k[j]);"),
     ("sort_int32_unsigned", "        return k ^ 0x80000000u;\n    if (dtype == OR_FLOAT32)",
