@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
 ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
-            "blockscans", "sort")
+            "blockscans", "sort", "select")
 DEFAULT_LEGS = ALL_LEGS
 
 
@@ -207,6 +207,24 @@ def main():
                    lambda a, b, thr=thr: ps.compact_if(a, "lt", thr, out=b, count=cnt), n,
                    4 * n + 4 * kept)
         del xs, xh
+    if "select" in legs:
+        # compaction by a byte flag array, and index selection, 2^27 elements, half kept
+        n = wl.SIZES["compact"]
+        xh = wl.compact_input()
+        fh = (wl.u32_bits(n, seed=77) & 1).astype(np.uint8)
+        kept = int(np.count_nonzero(fh))
+        xs = rotating(lambda i: to_dev(xh), sets=2)
+        fd = to_dev(fh)
+        cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        bw_leg("compact_flags_i32_2e27_sel50", xs,
+               lambda a, b: ps.compact_flags(a, fd, out=b, count=cnt), n, 5 * n + 4 * kept)
+        bw_leg("select_indices_flags_2e27_sel50", xs,
+               lambda a, b: ps.select_indices_flags(fd, out=b, count=cnt), n, n + 4 * kept)
+        thr = wl.threshold_for(0.5)
+        kept = int(np.count_nonzero(xh < thr))
+        bw_leg("select_indices_if_i32_2e27_sel50", xs,
+               lambda a, b: ps.select_indices_if(a, "lt", thr, out=b, count=cnt), n, 4 * n + 4 * kept)
+        del xs, xh, fh, fd
     if "rows64" in legs:
         xs = rotating(lambda i: to_dev(wl.rows64()))
         n = xs[0].numel()

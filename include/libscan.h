@@ -172,6 +172,29 @@ ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t *bytes);
 ls_status compact_if(const void *in, void *out, int64_t *count, int64_t n, ls_dtype t, ls_cmp cmp,
                      uint32_t threshold_bits, void *ws, size_t ws_bytes, void *stream);
 
+/* Stable compaction by a flag array ([SIMT3] 4.1-4.2: the input comes with a
+ * per-element validity mask; kept elements go to the front of the output in
+ * order and the count is computed on the device).
+ *   in, out   n 32-bit elements (any type; bits are copied); must not overlap.
+ *   flags     n bytes, nonzero = keep; any alignment; must not overlap out.
+ *   count     device int64_t, written with the number kept.
+ *   ws        >= ls_compact_workspace_bytes(n, LS_UINT32, ...) bytes.
+ * Cells of out at index >= *count are not written. */
+ls_status compact_flags(const void *in, const uint8_t *flags, void *out, int64_t *count, int64_t n,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Index selection: the positions i (uint32, ascending) of the elements that
+ * compact_if would keep, i.e. the output index of the compaction's scatter
+ * read the other way round ([Scan3] 一).  n < 2^32.  Other arguments as for
+ * compact_if; out_indices holds n uint32 and must not overlap in. */
+ls_status select_indices_if(const void *in, uint32_t *out_indices, int64_t *count, int64_t n,
+                            ls_dtype t, ls_cmp cmp, uint32_t threshold_bits, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* The positions i (uint32, ascending) with flags[i] != 0.  n < 2^32. */
+ls_status select_indices_flags(const uint8_t *flags, uint32_t *out_indices, int64_t *count,
+                               int64_t n, void *ws, size_t ws_bytes, void *stream);
+
 /* Row-wise scan of a rows x cols row-major, contiguous matrix: each row is
  * scanned on its own, with no carry between rows (the uniform-length case of a
  * segmented scan, [Blog2] 7.2).

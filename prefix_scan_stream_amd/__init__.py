@@ -22,7 +22,8 @@ __all__ = [
     "LibscanError", "library_path", "load_library", "ls_abi_version", "ls_status_string",
     "ls_scan_workspace_bytes", "ls_compact_workspace_bytes", "scan_inclusive", "scan_exclusive",
     "compact_if", "batched_row_scan", "workspace_for", "scan_ex", "ls_scan_ex_workspace_bytes",
-    "batched_row_scan_ex", "radix_sort", "ls_radix_sort_workspace_bytes",
+    "batched_row_scan_ex", "radix_sort", "ls_radix_sort_workspace_bytes", "compact_flags",
+    "select_indices_if", "select_indices_flags",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +85,12 @@ def load_library():
         lib.scan_ex.restype = I
         lib.batched_row_scan_ex.argtypes = [P, P, I64, I64, I, I, I, I, P]
         lib.batched_row_scan_ex.restype = I
+        lib.compact_flags.argtypes = [P, P, P, P, I64, P, SZ, P]
+        lib.compact_flags.restype = I
+        lib.select_indices_if.argtypes = [P, P, P, I64, I, I, U32, P, SZ, P]
+        lib.select_indices_if.restype = I
+        lib.select_indices_flags.argtypes = [P, P, P, I64, P, SZ, P]
+        lib.select_indices_flags.restype = I
         lib.ls_radix_sort_workspace_bytes.argtypes = [I64, I, I, ctypes.POINTER(SZ)]
         lib.ls_radix_sort_workspace_bytes.restype = I
         lib.radix_sort.argtypes = [P, P, P, P, I64, I, P, SZ, P]
@@ -249,8 +256,7 @@ def compact_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | None = 
         count = torch.empty(1, dtype=torch.int64, device=x.device)
     if count.dtype != torch.int64:
         raise ValueError("libscan: count must be int64")
-    np_dt = {"int32": "i4", "uint32": "u4", "float32": "f4"}[dt]
-    thr_bits = int(np.array([threshold], dtype=np_dt).view(np.uint32)[0])
+    thr_bits = _threshold_bits(dt, threshold)
     n = x.numel()
     stream, sh = _stream_handle(x.device)
     need = ls_compact_workspace_bytes(n, dt)
@@ -258,6 +264,85 @@ def compact_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | None = 
     st = lib.compact_if(_ptr(x), _ptr(out), _ptr(count), n, DTYPE_CODES[dt], CMP_CODES[cmp],
                         thr_bits, _ptr(ws), ws.numel(), sh)
     _check(st, "compact_if")
+    return out, count
+
+
+def _threshold_bits(dt: str, threshold) -> int:
+    np_dt = {"int32": "i4", "uint32": "u4", "float32": "f4"}[dt]
+    return int(np.array([threshold], dtype=np_dt).view(np.uint32)[0])
+
+
+def _count_tensor(count, device):
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=device)
+    if count.dtype != torch.int64:
+        raise ValueError("libscan: count must be int64")
+    return count
+
+
+def _flags_tensor(flags: torch.Tensor, n: int) -> torch.Tensor:
+    if flags.dtype not in (torch.uint8, torch.bool, torch.int8) or flags.numel() != n:
+        raise ValueError("libscan: flags must be n bytes (uint8 / bool)")
+    if not flags.is_contiguous():
+        raise ValueError("libscan: flags must be contiguous")
+    return flags
+
+
+def compact_flags(x: torch.Tensor, flags: torch.Tensor, out: torch.Tensor | None = None,
+                  count: torch.Tensor | None = None):
+    """Stable compaction of the 32-bit elements of x whose byte flag is nonzero.
+    Returns (out, count) like compact_if."""
+    lib = load_library()
+    _require_gpu(x, flags, out, count)
+    if not x.is_contiguous() or x.element_size() != 4:
+        raise ValueError("libscan: x must be a contiguous tensor of 32-bit elements")
+    n = x.numel()
+    flags = _flags_tensor(flags, n)
+    if out is None:
+        out = torch.empty_like(x)
+    count = _count_tensor(count, x.device)
+    stream, sh = _stream_handle(x.device)
+    ws = workspace_for(x.device, stream, ls_compact_workspace_bytes(n, "uint32"))
+    st = lib.compact_flags(_ptr(x), _ptr(flags), _ptr(out), _ptr(count), n, _ptr(ws), ws.numel(), sh)
+    _check(st, "compact_flags")
+    return out, count
+
+
+def select_indices_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | None = None,
+                      count: torch.Tensor | None = None):
+    """Positions (int32 tensor holding uint32 values) of the elements with
+    (x CMP threshold), ascending; returns (indices, count)."""
+    lib = load_library()
+    _require_gpu(x, out, count)
+    if not x.is_contiguous():
+        raise ValueError("libscan: input must be contiguous")
+    dt = _dtype_of(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=x.device)
+    count = _count_tensor(count, x.device)
+    stream, sh = _stream_handle(x.device)
+    ws = workspace_for(x.device, stream, ls_compact_workspace_bytes(n, dt))
+    st = lib.select_indices_if(_ptr(x), _ptr(out), _ptr(count), n, DTYPE_CODES[dt], CMP_CODES[cmp],
+                               _threshold_bits(dt, threshold), _ptr(ws), ws.numel(), sh)
+    _check(st, "select_indices_if")
+    return out, count
+
+
+def select_indices_flags(flags: torch.Tensor, out: torch.Tensor | None = None,
+                         count: torch.Tensor | None = None):
+    """Positions (int32 tensor holding uint32 values) of the nonzero flag bytes."""
+    lib = load_library()
+    _require_gpu(flags, out, count)
+    n = flags.numel()
+    flags = _flags_tensor(flags, n)
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=flags.device)
+    count = _count_tensor(count, flags.device)
+    stream, sh = _stream_handle(flags.device)
+    ws = workspace_for(flags.device, stream, ls_compact_workspace_bytes(n, "uint32"))
+    st = lib.select_indices_flags(_ptr(flags), _ptr(out), _ptr(count), n, _ptr(ws), ws.numel(), sh)
+    _check(st, "select_indices_flags")
     return out, count
 
 

@@ -47,7 +47,7 @@ def _compile(src: str) -> str:
     if src.endswith(".hip"):
         cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, f"--offload-arch={ARCH}", "-c", path, "-o", obj]
     subprocess.check_call(cmd)
     return obj
 

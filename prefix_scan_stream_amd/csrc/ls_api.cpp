@@ -69,6 +69,44 @@ ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Shared checks of the compaction family.  in may be NULL when has_in is false;
+// flags when has_flags is false.
+ls_status compact_common(const void* in, const uint8_t* flags, void* out, int64_t* count,
+                                int64_t n, ls_dtype t, ls_cmp cmp, uint32_t thr, int src, int pay,
+                                void* ws, size_t ws_bytes, void* stream)
+{
+    const bool has_in = src == 0 || pay == 0;
+    const bool has_flags = src == 1;
+    if (!size_ok(n) || !valid_dtype(t) || !valid_cmp(cmp) || count == nullptr || !aligned(count, 8))
+        return LS_ERR_INVALID_ARG;
+    if (pay == 1 && n > int64_t(UINT32_MAX))
+        return LS_ERR_INVALID_ARG;
+    const size_t bytes = size_t(n) * 4;
+    const size_t fbytes = has_flags ? size_t(n) : 0;
+    const size_t ibytes = has_in ? bytes : 0;
+    if (n > 0) {
+        if (out == nullptr || !aligned(out, 4))
+            return LS_ERR_INVALID_ARG;
+        if (has_in && (in == nullptr || !aligned(in, 4)))
+            return LS_ERR_INVALID_ARG;
+        if (has_flags && flags == nullptr)
+            return LS_ERR_INVALID_ARG;
+        if (overlaps(in, ibytes, out, bytes) || overlaps(flags, fbytes, out, bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (overlaps(count, 8, in, ibytes) || overlaps(count, 8, out, bytes) || overlaps(count, 8, flags, fbytes))
+        return LS_ERR_INVALID_ARG;
+    const size_t need = ls::compact_workspace_bytes(n);
+    ls_status st = check_ws(ws, ws_bytes, need);
+    if (st != LS_OK)
+        return st;
+    if (!aligned(ws, 16) || overlaps(ws, need, in, ibytes) || overlaps(ws, need, out, bytes) ||
+        overlaps(ws, need, count, 8) || overlaps(ws, need, flags, fbytes))
+        return LS_ERR_INVALID_ARG;
+    return from_hip(ls::launch_compact_general(has_in ? in : nullptr, flags, out, count, n, int(t), int(cmp),
+                                               thr, src, pay, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,26 +174,27 @@ ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t* bytes)
 ls_status compact_if(const void* in, void* out, int64_t* count, int64_t n, ls_dtype t, ls_cmp cmp,
                      uint32_t threshold_bits, void* ws, size_t ws_bytes, void* stream)
 {
-    if (!size_ok(n) || !valid_dtype(t) || !valid_cmp(cmp) || count == nullptr || !aligned(count, 8))
-        return LS_ERR_INVALID_ARG;
-    const size_t bytes = size_t(n) * 4;
-    if (n > 0) {
-        if (in == nullptr || out == nullptr || !aligned(in, 4) || !aligned(out, 4))
-            return LS_ERR_INVALID_ARG;
-        if (overlaps(in, bytes, out, bytes))
-            return LS_ERR_INVALID_ARG;
-    }
-    if (overlaps(count, 8, in, bytes) || overlaps(count, 8, out, bytes))
-        return LS_ERR_INVALID_ARG;
-    const size_t need = ls::compact_workspace_bytes(n);
-    ls_status st = check_ws(ws, ws_bytes, need);
-    if (st != LS_OK)
-        return st;
-    if (!aligned(ws, 16) || overlaps(ws, need, in, bytes) || overlaps(ws, need, out, bytes) ||
-        overlaps(ws, need, count, 8))
-        return LS_ERR_INVALID_ARG;
-    return from_hip(ls::launch_compact(in, out, count, n, int(t), int(cmp), threshold_bits, ws,
-                                       reinterpret_cast<hipStream_t>(stream)));
+    return compact_common(in, nullptr, out, count, n, t, cmp, threshold_bits, 0, 0, ws, ws_bytes, stream);
+}
+
+ls_status compact_flags(const void* in, const uint8_t* flags, void* out, int64_t* count, int64_t n,
+                        void* ws, size_t ws_bytes, void* stream)
+{
+    return compact_common(in, flags, out, count, n, LS_UINT32, LS_LT, 0, 1, 0, ws, ws_bytes, stream);
+}
+
+ls_status select_indices_if(const void* in, uint32_t* out_indices, int64_t* count, int64_t n, ls_dtype t,
+                            ls_cmp cmp, uint32_t threshold_bits, void* ws, size_t ws_bytes, void* stream)
+{
+    return compact_common(in, nullptr, out_indices, count, n, t, cmp, threshold_bits, 0, 1, ws, ws_bytes,
+                          stream);
+}
+
+ls_status select_indices_flags(const uint8_t* flags, uint32_t* out_indices, int64_t* count, int64_t n,
+                               void* ws, size_t ws_bytes, void* stream)
+{
+    return compact_common(nullptr, flags, out_indices, count, n, LS_UINT32, LS_LT, 0, 1, 1, ws, ws_bytes,
+                          stream);
 }
 
 static ls_status batched_common(const void* in, void* out, int64_t rows, int64_t cols, ls_dtype t,

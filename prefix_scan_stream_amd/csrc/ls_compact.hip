@@ -47,12 +47,17 @@ __device__ __forceinline__ uint32_t pred_bit(uint32_t v, uint32_t t, uint32_t ta
     return (table >> state) & 1u;
 }
 
-template <int DT, bool VEC>
+// What decides the keep bit, and what is written for a kept element.
+enum CompactSrc : int { SRC_CMP = 0, SRC_FLAGS = 1 };    // (x CMP thr) / flag byte != 0
+enum CompactPay : int { PAY_VALUE = 0, PAY_INDEX = 1 };  // x itself / its index (uint32)
+
+template <int DT, bool VEC, int SRC = SRC_CMP, int PAY = PAY_VALUE, bool FLAG4 = true>
 __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __restrict__ in,
                                                            uint32_t* __restrict__ out, int64_t n,
                                                            int64_t num_tiles, uint32_t thr,
                                                            uint32_t table, WsHeader* hdr,
-                                                           uint64_t* status, int64_t* count)
+                                                           uint64_t* status, int64_t* count,
+                                                           const uint8_t* __restrict__ flags)
 {
     constexpr int PARTS = CP_CHUNKS * CP_WAVES;  // (run, wave) kept counts per tile
     constexpr uint32_t RUN_STRIDE = CP_BLOCK * 16u;
@@ -77,20 +82,48 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
     const uint32_t voff = uint32_t(tid) * 16u;
 
-    // 1. load; predicate in registers (elements past n are never kept)
+    // 1. load; keep bits in registers (elements past n are never kept)
+    constexpr bool LOAD_VALUES = (SRC == SRC_CMP) || (PAY == PAY_VALUE);
     Run4<uint32_t> r[CP_CHUNKS];
     uint32_t keep[CP_CHUNKS];  // bit k: element k of the run is kept
+    if constexpr (LOAD_VALUES) {
 #pragma unroll
-    for (int j = 0; j < CP_CHUNKS; ++j)
-        r[j] = VEC ? load_run_x4<uint32_t>(rin, voff, j * RUN_STRIDE)
-                   : load_run_x1<uint32_t>(rin, voff, j * RUN_STRIDE);
+        for (int j = 0; j < CP_CHUNKS; ++j)
+            r[j] = VEC ? load_run_x4<uint32_t>(rin, voff, j * RUN_STRIDE)
+                       : load_run_x1<uint32_t>(rin, voff, j * RUN_STRIDE);
+    }
+    uint32_t fl[CP_CHUNKS];  // flag bytes of a run (SRC_FLAGS)
+    if constexpr (SRC == SRC_FLAGS) {
+        const __amdgpu_buffer_rsrc_t rfl = make_rsrc(flags + tbase, valid);
+#pragma unroll
+        for (int j = 0; j < CP_CHUNKS; ++j) {
+            const uint32_t b0 = 4u * uint32_t(j * CP_BLOCK + tid);
+            // a dword that straddles the end of the range would read as 0 as a whole,
+            // so the one run holding the last flag bytes of a ragged tile loads bytes
+            if (FLAG4 && (b0 + 4u <= valid || b0 >= valid)) {
+                fl[j] = __builtin_amdgcn_raw_buffer_load_b32(rfl, b0, 0, CACHE_NT);
+            } else {
+                uint32_t w = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(rfl, b0 + k, 0, CACHE_NT)) << (8 * k);
+                fl[j] = w;
+            }
+        }
+    }
 #pragma unroll
     for (int j = 0; j < CP_CHUNKS; ++j) {
         const uint32_t e0 = 4u * uint32_t(j * CP_BLOCK + tid);
         uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            m |= (e0 + k < valid ? pred_bit<DT>(r[j].v[k], thr, table) : 0u) << k;
+        for (int k = 0; k < 4; ++k) {
+            uint32_t b;
+            if constexpr (SRC == SRC_FLAGS)
+                b = ((fl[j] >> (8 * k)) & 0xffu) != 0u;
+            else
+                b = pred_bit<DT>(r[j].v[k], thr, table);
+            m |= (e0 + k < valid ? b : 0u) << k;
+        }
         keep[j] = m;
     }
 
@@ -129,7 +162,12 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (keep[j] & (1u << k))
-                s_items[rank++] = r[j].v[k];
+            {
+                if constexpr (PAY == PAY_INDEX)
+                    s_items[rank++] = uint32_t(tbase) + 4u * uint32_t(j * CP_BLOCK + tid) + k;
+                else
+                    s_items[rank++] = r[j].v[k];
+            }
         }
     }
 
@@ -212,8 +250,19 @@ static uint32_t truth_table(int cmp)
     return 0u;
 }
 
-hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, int dtype, int cmp,
-                          uint32_t thr, void* ws, hipStream_t s)
+template <int DT, bool VEC, int SRC, int PAY, bool FLAG4>
+static void launch_compact_kernel(dim3 grid, hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n,
+                                  int64_t tiles, uint32_t thr, uint32_t table, WsHeader* hdr,
+                                  uint64_t* status, int64_t* count, const uint8_t* flags)
+{
+    hipLaunchKernelGGL((compact_kernel<DT, VEC, SRC, PAY, FLAG4>), grid, dim3(CP_BLOCK), 0, s, in, out, n,
+                       tiles, thr, table, hdr, status, count, flags);
+}
+
+// src: SRC_CMP / SRC_FLAGS; pay: PAY_VALUE / PAY_INDEX
+hipError_t launch_compact_general(const void* in, const uint8_t* flags, void* out, int64_t* count,
+                                  int64_t n, int dtype, int cmp, uint32_t thr, int src, int pay,
+                                  void* ws, hipStream_t s)
 {
     if (n == 0) {
         hipLaunchKernelGGL(store_i64_kernel, dim3(1), dim3(64), 0, s, count, int64_t(0));
@@ -226,26 +275,44 @@ hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, 
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
     const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+    const bool flag4 = (reinterpret_cast<uintptr_t>(flags) & 3) == 0;
     const auto* pin = reinterpret_cast<const uint32_t*>(in);
     auto* pout = reinterpret_cast<uint32_t*>(out);
     const uint32_t table = truth_table(cmp);
-    const dim3 grid(static_cast<uint32_t>(tiles)), block(CP_BLOCK);
-#define LS_CP_LAUNCH(DT)                                                                          \
-    do {                                                                                          \
-        if (vec)                                                                                  \
-            hipLaunchKernelGGL((compact_kernel<DT, true>), grid, block, 0, s, pin, pout, n, tiles, \
-                               thr, table, hdr, status, count);                                   \
-        else                                                                                      \
-            hipLaunchKernelGGL((compact_kernel<DT, false>), grid, block, 0, s, pin, pout, n,      \
-                               tiles, thr, table, hdr, status, count);                            \
-    } while (0)
-    switch (dtype) {
-    case DT_INT32: LS_CP_LAUNCH(DT_INT32); break;
-    case DT_UINT32: LS_CP_LAUNCH(DT_UINT32); break;
-    default: LS_CP_LAUNCH(DT_FLOAT32); break;
+    const dim3 grid(static_cast<uint32_t>(tiles));
+#define LS_CP(DT, V, SRC, PAY, F4) \
+    launch_compact_kernel<DT, V, SRC, PAY, F4>(grid, s, pin, pout, n, tiles, thr, table, hdr, status, count, flags)
+    if (src == SRC_CMP) {
+        if (pay == PAY_VALUE) {
+            switch (dtype) {
+            case DT_INT32: if (vec) LS_CP(DT_INT32, true, SRC_CMP, PAY_VALUE, true); else LS_CP(DT_INT32, false, SRC_CMP, PAY_VALUE, true); break;
+            case DT_UINT32: if (vec) LS_CP(DT_UINT32, true, SRC_CMP, PAY_VALUE, true); else LS_CP(DT_UINT32, false, SRC_CMP, PAY_VALUE, true); break;
+            default: if (vec) LS_CP(DT_FLOAT32, true, SRC_CMP, PAY_VALUE, true); else LS_CP(DT_FLOAT32, false, SRC_CMP, PAY_VALUE, true); break;
+            }
+        } else {
+            switch (dtype) {
+            case DT_INT32: if (vec) LS_CP(DT_INT32, true, SRC_CMP, PAY_INDEX, true); else LS_CP(DT_INT32, false, SRC_CMP, PAY_INDEX, true); break;
+            case DT_UINT32: if (vec) LS_CP(DT_UINT32, true, SRC_CMP, PAY_INDEX, true); else LS_CP(DT_UINT32, false, SRC_CMP, PAY_INDEX, true); break;
+            default: if (vec) LS_CP(DT_FLOAT32, true, SRC_CMP, PAY_INDEX, true); else LS_CP(DT_FLOAT32, false, SRC_CMP, PAY_INDEX, true); break;
+            }
+        }
+    } else {
+        if (pay == PAY_VALUE) {
+            if (vec) { if (flag4) LS_CP(DT_UINT32, true, SRC_FLAGS, PAY_VALUE, true); else LS_CP(DT_UINT32, true, SRC_FLAGS, PAY_VALUE, false); }
+            else { if (flag4) LS_CP(DT_UINT32, false, SRC_FLAGS, PAY_VALUE, true); else LS_CP(DT_UINT32, false, SRC_FLAGS, PAY_VALUE, false); }
+        } else {
+            if (vec) { if (flag4) LS_CP(DT_UINT32, true, SRC_FLAGS, PAY_INDEX, true); else LS_CP(DT_UINT32, true, SRC_FLAGS, PAY_INDEX, false); }
+            else { if (flag4) LS_CP(DT_UINT32, false, SRC_FLAGS, PAY_INDEX, true); else LS_CP(DT_UINT32, false, SRC_FLAGS, PAY_INDEX, false); }
+        }
     }
-#undef LS_CP_LAUNCH
+#undef LS_CP
     return hipGetLastError();
+}
+
+hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, int dtype, int cmp,
+                          uint32_t thr, void* ws, hipStream_t s)
+{
+    return launch_compact_general(in, nullptr, out, count, n, dtype, cmp, thr, SRC_CMP, PAY_VALUE, ws, s);
 }
 
 }  // namespace ls

@@ -27,6 +27,10 @@ int64_t compact_tile_elems();
 size_t compact_workspace_bytes(int64_t n);
 hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, int dtype, int cmp,
                           uint32_t threshold_bits, void* ws, hipStream_t stream);
+// src: 0 = predicate (x CMP threshold), 1 = flag bytes; pay: 0 = values, 1 = uint32 indices
+hipError_t launch_compact_general(const void* in, const uint8_t* flags, void* out, int64_t* count,
+                                  int64_t n, int dtype, int cmp, uint32_t threshold_bits, int src,
+                                  int pay, void* ws, hipStream_t stream);
 
 // ---- batched row scan (ls_batched.hip)
 // kind: the block-level scan (ls_block_scan values); 0 = wave DPP, the default.

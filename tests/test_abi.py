@@ -182,6 +182,32 @@ def test_compact_validation(lib):
     assert call(n=1 << 20, wsb=256) == WS
 
 
+def test_flags_and_indices_validation(lib):
+    A_F = 0x7F0060000000
+
+    def cf(inp=A_IN, flags=A_F, out=A_OUT, count=A_TOT, n=10, ws=A_WS, wsb=BIG_WS):
+        return lib.compact_flags(inp, flags, out, count, n, ws, wsb, None)
+
+    assert cf(n=-1) == INV
+    assert cf(flags=None) == INV
+    assert cf(inp=None) == INV
+    assert cf(out=A_IN) == INV
+    assert cf(flags=A_OUT + 3) == INV          # flags overlap out
+    assert cf(count=None) == INV
+    assert cf(ws=None) == WS
+    assert cf(flags=A_F + 1, ws=None) == WS    # any flag alignment is accepted
+
+    def si(inp=A_IN, out=A_OUT, n=10, t=INT32, cmp=0):
+        return lib.select_indices_if(inp, out, A_TOT, n, t, cmp, 0, A_WS, BIG_WS, None)
+
+    assert si(n=1 << 32) == INV                # indices are uint32
+    assert si(cmp=9) == INV
+    assert si(inp=None) == INV
+    assert lib.select_indices_flags(None, A_OUT, A_TOT, 10, A_WS, BIG_WS, None) == INV
+    assert lib.select_indices_flags(A_F, A_OUT, A_TOT, 1 << 32, A_WS, BIG_WS, None) == INV
+    assert lib.select_indices_flags(A_F, A_OUT, A_TOT, 10, None, 0, None) == WS
+
+
 def test_batched_validation(lib):
     def call(inp=A_IN, out=A_OUT, rows=4, cols=64, t=F32, op=SUM, excl=1):
         return lib.batched_row_scan(inp, out, rows, cols, t, op, excl, None)
