@@ -149,7 +149,7 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
             s_part[lane] = inc - v;
         if (lane == 0) {
             s_kept = kept;
-            status_store(status + tile, CountCodec::pack(tile == 0 ? ST_PREFIX : ST_AGGREGATE, kept));
+            status_store(status_word(status, tile), CountCodec::pack(tile == 0 ? ST_PREFIX : ST_AGGREGATE, kept));
         }
     }
     __syncthreads();
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __res
         if (tile != 0) {
             base = int64_t(lookback<CountCodec>(status, tile, hdr));
             if (lane == 0)
-                status_store(status + tile, CountCodec::pack(ST_PREFIX, uint64_t(base) + kept));
+                status_store(status_word(status, tile), CountCodec::pack(ST_PREFIX, uint64_t(base) + kept));
         }
         if (lane == 0)
             s_base = base;
@@ -232,7 +232,7 @@ size_t compact_workspace_bytes(int64_t n)
     int64_t tiles = cp_tiles(n);
     if (tiles < 1)
         tiles = 1;
-    size_t bytes = sizeof(WsHeader) + size_t(tiles) * sizeof(uint64_t);
+    size_t bytes = sizeof(WsHeader) + size_t(tiles) * STATUS_SLOT_BYTES;
     return (bytes + 255) & ~size_t(255);
 }
 

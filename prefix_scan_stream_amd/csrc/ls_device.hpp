@@ -260,8 +260,19 @@ __device__ __forceinline__ void store_run(T* __restrict__ p, int64_t idx, int64_
 // scope makes the accesses coherent across the eight XCDs (their L2s are not).
 //   32-bit payload (scans): bits 63..32 = flag, bits 31..0 = value bits.
 //   62-bit payload (compaction counts): bits 63..62 = flag, bits 61..0 = count.
+// Each tile's word sits alone in a 256-byte slot.  Packed eight to a cache line,
+// the words of neighbouring tiles are published and polled by hundreds of waves
+// at once through one line; measured on MI355X that contention slowed the whole
+// data stream (int32 scan of 2^28: 433 us packed, 398 us with one word per
+// 256 bytes).  The cost is 256 bytes of workspace per tile.
 enum : uint32_t { ST_EMPTY = 0, ST_AGGREGATE = 1, ST_PREFIX = 2 };
+constexpr int STATUS_STRIDE = 32;                          // 64-bit words per tile slot
+constexpr size_t STATUS_SLOT_BYTES = 8 * STATUS_STRIDE;    // workspace bytes per tile
 
+__device__ __forceinline__ uint64_t* status_word(uint64_t* status, int64_t tile)
+{
+    return status + tile * STATUS_STRIDE;
+}
 __device__ __forceinline__ void status_store(uint64_t* p, uint64_t w)
 {
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -345,62 +356,55 @@ struct CountCodec {
 };
 
 // Exclusive prefix of tile `tile` (>= 1), computed by one full wave from the
-// tile status words.  Each poll reads a window of LB_WINDOW tiles (256 by
-// default), lane l holding tiles base + 4l .. base + 4l + 3, so one memory round trip covers four
-// times what one word per lane would; the window size bounds how fast the chain
-// of full prefixes can advance (tiles per round trip).  In the window, the
-// newest tile that has published a full prefix ends the walk: the answer is the
-// operator over it and every newer tile of the window.  Without one, all 256
-// totals are combined and the window moves 256 tiles back.  An empty word newer
-// than the stopping tile means that tile has not published yet: poll again.
-#ifndef LS_LB_PER_LANE
-#define LS_LB_PER_LANE 1
-#endif
-constexpr int LB_PER_LANE = LS_LB_PER_LANE;
-constexpr int LB_WINDOW = 64 * LB_PER_LANE;
+// tile status words.  A poll reads a window of 64 tiles, lane l holding tile
+// last - 63 + l.  In the window, the newest tile that has published a full
+// prefix ends the walk: the answer is the operator over it and every newer tile
+// of the window.  Without one, the 64 totals are combined and the window moves
+// 64 tiles back.  An empty word newer than the stopping tile means that tile has
+// not published yet: sleep, then poll again.  The first poll reads only the
+// eight nearest tiles (one 64-byte request per lane group instead of 64 slots),
+// which settles most tiles whose predecessor is already done.  Windows of 128 to
+// 512 words per poll and shorter sleeps were measured slower: the polls
+// themselves load the memory system that the tiles' data also goes through.
+constexpr int LB_WINDOW = 64;
+constexpr int LB_NEAR = 8;      // tiles read by the first, narrow poll
+constexpr int LB_SLEEP = 32;    // s_sleep units (64 clocks each) between polls
 
 template <class Codec>
 __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHeader* hdr)
 {
     using V = typename Codec::V;
     const int lane = lane_id();
+    auto word = [&](int64_t idx) -> uint64_t {
+        return idx >= 0 ? status_load(status + idx * STATUS_STRIDE) : Codec::pack(ST_PREFIX, Codec::identity());
+    };
+    {
+        // narrow first poll: lanes 56..63 read the eight nearest tiles; the
+        // other lanes stand for tiles that do not take part (identity totals)
+        const bool near = lane >= LB_WINDOW - LB_NEAR;
+        const uint64_t w = near ? word(tile - LB_WINDOW + lane) : Codec::pack(ST_AGGREGATE, Codec::identity());
+        const uint64_t has = __ballot(near && Codec::flag(w) == ST_PREFIX);
+        const int hi = has ? 63 - __builtin_clzll(has) : -1;
+        if (hi >= 0 && !__ballot(lane > hi && Codec::flag(w) == ST_EMPTY))
+            return Codec::wave_reduce(lane >= hi ? Codec::value(w) : Codec::identity(), hi);
+    }
     V excl = Codec::identity();
     int64_t last = tile - 1;
     int spins = 0;
     for (;;) {
-        const int64_t base = last - (LB_WINDOW - 1) + LB_PER_LANE * lane;
-        uint64_t w[LB_PER_LANE];
-#pragma unroll
-        for (int q = 0; q < LB_PER_LANE; ++q) {
-            const int64_t idx = base + q;
-            w[q] = (idx >= 0) ? status_load(status + idx) : Codec::pack(ST_PREFIX, Codec::identity());
-        }
-        int lq = -1;  // newest tile of this lane with a full prefix
-#pragma unroll
-        for (int q = 0; q < LB_PER_LANE; ++q)
-            if (Codec::flag(w[q]) == ST_PREFIX)
-                lq = q;
-        const uint64_t has = __ballot(lq >= 0);
+        const uint64_t w = word(last - (LB_WINDOW - 1) + lane);
+        const uint64_t has = __ballot(Codec::flag(w) == ST_PREFIX);
         const int hi = has ? 63 - __builtin_clzll(has) : -1;
-        const int stop = hi >= 0 ? LB_PER_LANE * hi + __builtin_amdgcn_readlane(lq, hi) : -1;
-        bool waiting = false;
-#pragma unroll
-        for (int q = 0; q < LB_PER_LANE; ++q)
-            waiting |= (LB_PER_LANE * lane + q > stop) && Codec::flag(w[q]) == ST_EMPTY;
-        if (__ballot(waiting)) {
+        if (__ballot(lane > hi && Codec::flag(w) == ST_EMPTY)) {
             if (++spins < LOOKBACK_SPIN_LIMIT) {
-                __builtin_amdgcn_s_sleep(1);
+                __builtin_amdgcn_s_sleep(LB_SLEEP);
                 continue;
             }
             if (lane == 0)
                 flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
             return excl;  // only reached on a defect; the error word reports it
         }
-        V part = Codec::identity();
-#pragma unroll
-        for (int q = 0; q < LB_PER_LANE; ++q)
-            if (LB_PER_LANE * lane + q >= stop)
-                part = Codec::apply(part, Codec::value(w[q]));
+        const V part = lane >= hi ? Codec::value(w) : Codec::identity();
         excl = Codec::apply(Codec::wave_reduce(part, hi), excl);  // older tiles on the left
         if (hi >= 0)
             return excl;

@@ -15,8 +15,8 @@ enum OpCode : int { OP_SUM = 0, OP_MAX = 1, OP_XOR = 2 };
 enum Scheme : int { SCHEME_SINGLE_PASS = 0, SCHEME_REDUCE_THEN_SCAN = 1, SCHEME_SCAN_THEN_PROPAGATE = 2 };
 
 // ---- single-pass device-wide scan (ls_scan.hip)
-// Zeroes the workspace header and `status_words` tile status words after it.
-hipError_t clear_workspace(void* ws, int64_t status_words, hipStream_t stream);
+// Zeroes the workspace header and the status word of each of `tiles` tile slots.
+hipError_t clear_workspace(void* ws, int64_t tiles, hipStream_t stream);
 int64_t scan_tile_elems();
 size_t scan_workspace_bytes(int64_t n, int scheme);
 hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, bool inclusive,

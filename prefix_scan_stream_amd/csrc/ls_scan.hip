@@ -118,10 +118,10 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
                 status_store(status, Codec::pack(ST_PREFIX, agg));
         } else {
             if (lane == 0)
-                status_store(status + tile, Codec::pack(ST_AGGREGATE, agg));
+                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
             p = lookback<Codec>(status, tile, hdr);
             if (lane == 0)
-                status_store(status + tile, Codec::pack(ST_PREFIX, Op::apply(p, agg)));
+                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg)));
         }
         if (lane < PARTS)
             s_part[lane] = Op::apply(p, exc);
@@ -320,11 +320,16 @@ __global__ void write_total_kernel(const typename Op::T* seeds, const typename O
 }
 
 // Clears the workspace header and the first `words` status words.
-__global__ __launch_bounds__(256) void ws_clear_kernel(uint4* p, int64_t n16)
+// Zeroes the workspace header and the status word of every tile slot (the rest
+// of a slot is never read).  A kernel, not a memset, so the call can be captured
+// in a graph.
+__global__ __launch_bounds__(256) void ws_clear_kernel(uint32_t* hdr_words, uint64_t* status, int64_t tiles)
 {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i < n16)
-        p[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < int64_t(sizeof(WsHeader) / 4))
+        hdr_words[i] = 0u;
+    if (i < tiles)
+        status[i * STATUS_STRIDE] = 0u;
 }
 
 __global__ void store_u32_kernel(uint32_t* p, uint32_t v)
@@ -351,7 +356,7 @@ size_t scan_workspace_bytes(int64_t n, int scheme)
 {
     if (scheme == SCHEME_SINGLE_PASS) {
         const int64_t sp = single_pass_tiles(n);
-        return round256(sizeof(WsHeader) + size_t(sp < 1 ? 1 : sp) * sizeof(uint64_t));
+        return round256(sizeof(WsHeader) + size_t(sp < 1 ? 1 : sp) * STATUS_SLOT_BYTES);
     }
     int64_t tiles = num_tiles_for(n);
     if (tiles < 1)
@@ -362,13 +367,13 @@ size_t scan_workspace_bytes(int64_t n, int scheme)
     return bytes;
 }
 
-hipError_t clear_workspace(void* ws, int64_t status_words, hipStream_t s)
+hipError_t clear_workspace(void* ws, int64_t tiles, hipStream_t s)
 {
-    const int64_t bytes = int64_t(sizeof(WsHeader)) + status_words * 8;
-    const int64_t n16 = (bytes + 15) / 16;
-    const int64_t blocks = (n16 + 255) / 256;
+    const int64_t n = tiles > int64_t(sizeof(WsHeader) / 4) ? tiles : int64_t(sizeof(WsHeader) / 4);
+    const int64_t blocks = (n + 255) / 256;
+    auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
     hipLaunchKernelGGL(ws_clear_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<uint4*>(ws), n16);
+                       reinterpret_cast<uint32_t*>(ws), status, tiles);
     return hipGetLastError();
 }
 

@@ -60,10 +60,10 @@ def test_workspace_queries(lib):
     b0 = ps.ls_scan_workspace_bytes(0, "int32", "sum")
     b1 = ps.ls_scan_workspace_bytes(1 << 28, "int32", "sum")
     assert b0 > 0 and b0 % 256 == 0 and b1 % 256 == 0
-    # a 256-byte header plus one 8-byte status word per tile of at least 1024 elements
-    assert b0 < b1 <= 256 + 8 * ((1 << 28) // 1024) + 256
+    # a 256-byte header plus one 256-byte status slot per tile of at least 8192 elements
+    assert b0 < b1 <= 256 + 256 * ((1 << 28) // 8192) + 256
     c1 = ps.ls_compact_workspace_bytes(1 << 27, "int32")
-    assert ps.ls_compact_workspace_bytes(0, "int32") < c1 <= 256 + 8 * ((1 << 27) // 1024) + 256
+    assert ps.ls_compact_workspace_bytes(0, "int32") < c1 <= 256 + 256 * ((1 << 27) // 8192) + 256
     sz = ctypes.c_size_t(0)
     assert lib.ls_scan_workspace_bytes(-1, INT32, SUM, ctypes.byref(sz)) == INV
     assert lib.ls_scan_workspace_bytes(10, 7, SUM, ctypes.byref(sz)) == INV
