@@ -11,7 +11,8 @@ the C oracle on tiny inputs.
 
 Codes (independent of the library header):
   dtype  "int32" | "uint32" | "float32"
-  op     "sum" | "max" | "xor"
+  op     "sum" | "max" | "xor" | "min" | "and" | "or" | "prod" | "affine"
+         (float32: sum, max, min, prod; affine: uint32 only)
   cmp    "lt" | "le" | "gt" | "ge" | "eq" | "ne"
 """
 from __future__ import annotations
@@ -28,7 +29,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"int32": 0, "uint32": 1, "float32": 2}
-OPS = {"sum": 0, "max": 1, "xor": 2}
+OPS = {"sum": 0, "max": 1, "xor": 2, "min": 3, "and": 4, "or": 5, "prod": 6, "affine": 7}
 CMPS = {"lt": 0, "le": 1, "gt": 2, "ge": 3, "eq": 4, "ne": 5}
 
 _lock = threading.Lock()
@@ -57,6 +58,14 @@ def _bind(lib):
     lib.oracle_scan_f32_sum.restype = None
     lib.oracle_scan_f32_max.argtypes = [P, P, I64, I, P]
     lib.oracle_scan_f32_max.restype = None
+    lib.oracle_scan_f32_min.argtypes = [P, P, I64, I, P]
+    lib.oracle_scan_f32_min.restype = None
+    lib.oracle_scan_f32_prod.argtypes = [P, P, I64, I, P]
+    lib.oracle_scan_f32_prod.restype = None
+    lib.oracle_batched_f32_min.argtypes = [P, P, I64, I64, I]
+    lib.oracle_batched_f32_min.restype = None
+    lib.oracle_batched_f32_prod.argtypes = [P, P, I64, I64, I]
+    lib.oracle_batched_f32_prod.restype = None
     lib.oracle_compact.argtypes = [P, P, I64, I, I, U32]
     lib.oracle_compact.restype = I64
     lib.oracle_compact_via_scan.argtypes = [P, P, I64, I, I, U32, P, P]
@@ -156,10 +165,16 @@ class Oracle:
             tot = np.zeros(1, np.float64)
             lib.oracle_scan_f32_sum(_ptr(x), _ptr(y), _ptr(b), n, inc, _ptr(tot))
             return ScanResult(y, tot[0], b)
-        if op == "max":
+        if op in ("max", "min"):
             y = np.empty(n, np.float32)
             tot = np.zeros(1, np.float32)
-            lib.oracle_scan_f32_max(_ptr(x), _ptr(y), n, inc, _ptr(tot))
+            fn = lib.oracle_scan_f32_max if op == "max" else lib.oracle_scan_f32_min
+            fn(_ptr(x), _ptr(y), n, inc, _ptr(tot))
+            return ScanResult(y, tot[0])
+        if op == "prod":
+            y = np.empty(n, np.float64)
+            tot = np.zeros(1, np.float64)
+            lib.oracle_scan_f32_prod(_ptr(x), _ptr(y), n, inc, _ptr(tot))
             return ScanResult(y, tot[0])
         raise ValueError(f"oracle: op {op} is not defined for float32")
 
@@ -204,9 +219,14 @@ class Oracle:
             b = np.empty((rows, cols), np.float64)
             lib.oracle_batched_f32_sum(_ptr(x), _ptr(y), _ptr(b), rows, cols, inc)
             return ScanResult(y, None, b)
-        if op == "max":
+        if op in ("max", "min"):
             y = np.empty((rows, cols), np.float32)
-            lib.oracle_batched_f32_max(_ptr(x), _ptr(y), rows, cols, inc)
+            fn = lib.oracle_batched_f32_max if op == "max" else lib.oracle_batched_f32_min
+            fn(_ptr(x), _ptr(y), rows, cols, inc)
+            return ScanResult(y, None)
+        if op == "prod":
+            y = np.empty((rows, cols), np.float64)
+            lib.oracle_batched_f32_prod(_ptr(x), _ptr(y), rows, cols, inc)
             return ScanResult(y, None)
         raise ValueError(f"oracle: op {op} is not defined for float32")
 

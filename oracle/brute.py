@@ -23,8 +23,18 @@ def _signed(v: int) -> int:
     return v - (1 << 32) if v & 0x80000000 else v
 
 
+def _mat2_mul(m, n):
+    """2x2 integer matrix product m @ n (lists of rows), entries mod 2^16."""
+    return [[(m[r][0] * n[0][c] + m[r][1] * n[1][c]) & 0xFFFF for c in range(2)] for r in range(2)]
+
+
+def _affine_to_mat(e):
+    return [[(e >> 16) & 0xFFFF, e & 0xFFFF], [0, 1]]
+
+
 def op_fn(dtype: str, op: str):
-    """Binary operator on Python ints holding 32-bit patterns (int32/uint32)."""
+    """Binary operator on Python ints holding 32-bit patterns (int32/uint32),
+    called as f(earlier, later)."""
     if op == "sum":
         return lambda a, b: (a + b) & M32
     if op == "xor":
@@ -33,12 +43,38 @@ def op_fn(dtype: str, op: str):
         if dtype == "int32":
             return lambda a, b: a if _signed(a) > _signed(b) else b
         return lambda a, b: a if (a & M32) > (b & M32) else b
+    if op == "min":
+        if dtype == "int32":
+            return lambda a, b: a if _signed(a) < _signed(b) else b
+        return lambda a, b: a if (a & M32) < (b & M32) else b
+    if op == "and":
+        return lambda a, b: a & b & M32
+    if op == "or":
+        return lambda a, b: (a | b) & M32
+    if op == "prod":
+        return lambda a, b: (a * b) & M32
+    if op == "affine" and dtype == "uint32":
+        # the map v -> a v + b as the matrix [[a, b], [0, 1]]; the later map is
+        # applied after the earlier one, so its matrix multiplies on the left
+        def f(a, b):
+            m = _mat2_mul(_affine_to_mat(b), _affine_to_mat(a))
+            assert m[1] == [0, 1]
+            return (m[0][0] << 16) | m[0][1]
+        return f
     raise ValueError(op)
 
 
 def identity(dtype: str, op: str) -> int:
     if op == "max":
         return 0x80000000 if dtype == "int32" else 0
+    if op == "min":
+        return 0x7FFFFFFF if dtype == "int32" else 0xFFFFFFFF
+    if op == "and":
+        return 0xFFFFFFFF
+    if op == "prod":
+        return 1
+    if op == "affine":
+        return 1 << 16
     return 0
 
 

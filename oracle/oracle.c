@@ -19,7 +19,8 @@
  *
  * Codes used below (defined here, independently of the library's header):
  *   dtype: 0 = int32, 1 = uint32, 2 = float32
- *   op:    0 = sum,   1 = max,    2 = xor
+ *   op:    0 = sum,   1 = max,    2 = xor,  3 = min,  4 = and,  5 = or,
+ *          6 = product,  7 = affine-map composition (uint32 only)
  *   cmp:   0 = <, 1 = <=, 2 = >, 3 = >=, 4 = ==, 5 = !=
  * Readings of points the pages leave open (operator identities, integer wrap,
  * tie rule of the float max) are stated at each routine.
@@ -34,6 +35,11 @@
 #define OR_SUM 0
 #define OR_MAX 1
 #define OR_XOR 2
+#define OR_MIN 3
+#define OR_AND 4
+#define OR_OR 5
+#define OR_PROD 6
+#define OR_AFFINE 7
 
 /* ---- the binary operators ------------------------------------------------
  * [Scan3] §一 (last paragraph) and §三: scan is defined for any associative
@@ -41,6 +47,28 @@
  * Integer addition wraps modulo 2^32 (two's complement), computed on uint32_t so
  * that C has no undefined behaviour; the pages never overflow, so any wrapping
  * rule agrees with them, and this one is what 32-bit hardware addition does. */
+/* [Blog2] §3.3 (generic operators) adds to these the product, min and the
+ * logical AND / OR; the integer product wraps modulo 2^32 like the sum.
+ *
+ * Affine-map composition ([Scan3] §三, last paragraph: any associative operator
+ * may be scanned, matrix chain products included, and a non-commutative one must
+ * keep its left-right order).  A uint32 element (a << 16) | b stands for the map
+ * v -> a*v + b (mod 2^16), i.e. the 2x2 matrix [[a, b], [0, 1]] acting on the
+ * column (v, 1).  Scanning applies the earlier map first: the element for
+ * x[0..i] is M_i * ... * M_1 * M_0, and combining an earlier e = (a1, b1) with a
+ * later f = (a2, b2) gives the map v -> a2*(a1*v + b1) + b2, i.e.
+ * (a2*a1, a2*b1 + b2), all mod 2^16.  Not commutative, so any slip in the order
+ * of a combination shows. */
+static uint32_t affine_then(uint32_t earlier, uint32_t later)
+{
+    uint32_t a1 = earlier >> 16, b1 = earlier & 0xffffu;
+    uint32_t a2 = later >> 16, b2 = later & 0xffffu;
+    uint32_t a = (a2 * a1) & 0xffffu;
+    uint32_t b = (a2 * b1 + b2) & 0xffffu;
+    return (a << 16) | b;
+}
+
+/* op(earlier, later): the scan's accumulator is always the left operand. */
 static uint32_t op_u32(int dtype, int op, uint32_t a, uint32_t b)
 {
     switch (op) {
@@ -52,22 +80,47 @@ static uint32_t op_u32(int dtype, int op, uint32_t a, uint32_t b)
         if (dtype == OR_INT32)
             return ((int32_t)a > (int32_t)b) ? a : b;
         return (a > b) ? a : b;
+    case OR_MIN:
+        if (dtype == OR_INT32)
+            return ((int32_t)a < (int32_t)b) ? a : b;
+        return (a < b) ? a : b;
+    case OR_AND:
+        return a & b;
+    case OR_OR:
+        return a | b;
+    case OR_PROD:
+        return a * b; /* wraps mod 2^32; the low 32 bits are the same for int32 */
+    case OR_AFFINE:
+        return affine_then(a, b);
     }
     return 0;
 }
 
 /* Identity of each operator: the value an exclusive scan puts in its first cell.
  * [Scan3] §一 fixes z[0] = 0 for addition; for max and xor the same role is
- * played by the operator's identity (0 for xor, the smallest value for max). */
+ * played by the operator's identity (0 for xor and or, the smallest value for
+ * max, the largest for min, all ones for and, 1 for the product, the identity
+ * map for affine maps). */
 static uint32_t identity_u32(int dtype, int op)
 {
-    if (op == OR_MAX)
-        return dtype == OR_INT32 ? 0x80000000u : 0u;
-    return 0u;
+    switch (op) {
+    case OR_MAX:
+        return dtype == OR_INT32 ? 0x80000000u : 0u; /* smallest value */
+    case OR_MIN:
+        return dtype == OR_INT32 ? 0x7fffffffu : 0xffffffffu; /* largest value */
+    case OR_AND:
+        return 0xffffffffu;
+    case OR_PROD:
+        return 1u;
+    case OR_AFFINE:
+        return 0x00010000u; /* v -> 1*v + 0 */
+    }
+    return 0u; /* sum, xor, or */
 }
 
-/* ---- integer scans (int32 / uint32; sum, max, xor) -------------------------
+/* ---- integer scans (int32 / uint32; every operator above) -------------------
  * Inclusive: y[i] = x[0] (+) ... (+) x[i]            [Scan3] §一, first formula
+ * ((+) is any of the operators above, earlier operand on the left)
  * Exclusive: z[0] = identity, z[i] = x[0] (+) ... (+) x[i-1]   [Scan3] §一
  * Serial evaluation: one accumulator carried left to right, exactly the serial
  * loop of [Scan3] §一 and [Blog2] §2.1.  The total (the value no exclusive cell
@@ -76,7 +129,9 @@ static uint32_t identity_u32(int dtype, int op)
 int oracle_scan_u32(const uint32_t *x, uint32_t *y, int64_t n, int dtype, int op,
                     int inclusive, uint32_t *total)
 {
-    if ((dtype != OR_INT32 && dtype != OR_UINT32) || op < OR_SUM || op > OR_XOR)
+    if ((dtype != OR_INT32 && dtype != OR_UINT32) || op < OR_SUM || op > OR_AFFINE)
+        return -1;
+    if (op == OR_AFFINE && dtype != OR_UINT32)
         return -1;
     uint32_t acc = identity_u32(dtype, op);
     if (inclusive) {
@@ -149,6 +204,55 @@ void oracle_scan_f32_max(const float *x, float *y, int64_t n, int inclusive, flo
         } else {
             y[i] = acc;
             acc = fmax_right(acc, x[i]);
+        }
+    }
+    if (total)
+        *total = acc;
+}
+
+/* ---- float32 min ------------------------------------------------------------
+ * min(a, b) = (a < b) ? a : b in float32: like the max, a tie (including -0
+ * against +0) keeps the right operand, so the rule is associative on non-NaN data
+ * and every association order gives the same bits.  Identity: +infinity. */
+static float fmin_right(float a, float b)
+{
+    return (a < b) ? a : b;
+}
+
+void oracle_scan_f32_min(const float *x, float *y, int64_t n, int inclusive, float *total)
+{
+    uint32_t pinf_bits = 0x7f800000u;
+    float acc;
+    memcpy(&acc, &pinf_bits, sizeof acc);
+    for (int64_t i = 0; i < n; ++i) {
+        if (inclusive) {
+            acc = (i == 0) ? x[0] : fmin_right(acc, x[i]);
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc = fmin_right(acc, x[i]);
+        }
+    }
+    if (total)
+        *total = acc;
+}
+
+/* ---- float32 product, accumulated in double ---------------------------------
+ * The running product of the elements ([Blog2] §3.3), carried in a double.  A
+ * float32 product of k factors evaluated in any association has a relative error
+ * of at most about (k-1) * 2^-24 (one rounding per multiplication), so the
+ * double result is the reference and the tolerance is relative. */
+void oracle_scan_f32_prod(const float *x, double *y, int64_t n, int inclusive, double *total)
+{
+    double acc = 1.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)x[i];
+        if (inclusive) {
+            acc = (i == 0) ? v : acc * v;
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc *= v;
         }
     }
     if (total)
@@ -265,6 +369,18 @@ void oracle_batched_f32_max(const float *x, float *y, int64_t rows, int64_t cols
 {
     for (int64_t r = 0; r < rows; ++r)
         oracle_scan_f32_max(x + r * cols, y + r * cols, cols, inclusive, 0);
+}
+
+void oracle_batched_f32_min(const float *x, float *y, int64_t rows, int64_t cols, int inclusive)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        oracle_scan_f32_min(x + r * cols, y + r * cols, cols, inclusive, 0);
+}
+
+void oracle_batched_f32_prod(const float *x, double *y, int64_t rows, int64_t cols, int inclusive)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        oracle_scan_f32_prod(x + r * cols, y + r * cols, cols, inclusive, 0);
 }
 
 /* ---- radix-sort order and stable sort --------------------------------------

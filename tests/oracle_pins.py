@@ -18,7 +18,14 @@ from conftest import load_golden
 from oracle import brute
 
 INT_DTYPES = ("int32", "uint32")
-OPS = ("sum", "max", "xor")
+OPS = ("sum", "max", "xor", "min", "and", "or", "prod", "affine")
+FLOAT_OPS = ("sum", "max", "min", "prod")
+
+
+def _defined(dtype, op):
+    if dtype == "float32":
+        return op in FLOAT_OPS
+    return op != "affine" or dtype == "uint32"
 M32 = 0xFFFFFFFF
 
 
@@ -87,6 +94,8 @@ def pin_inclusive_exclusive_relation(orc):
     rng = np.random.default_rng(11)
     for dtype in INT_DTYPES:
         for op in OPS:
+            if not _defined(dtype, op):
+                continue
             for n in (1, 2, 7, 100):
                 x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
                 x = x.view(np.int32) if dtype == "int32" else x
@@ -104,7 +113,7 @@ def pin_inclusive_exclusive_relation(orc):
 def pin_empty_input(orc):
     for dtype in INT_DTYPES + ("float32",):
         for op in OPS:
-            if dtype == "float32" and op == "xor":
+            if not _defined(dtype, op):
                 continue
             x = np.zeros(0, dtype)
             for inc in (True, False):
@@ -225,6 +234,8 @@ def pin_brute_force_random(orc):
     rng = np.random.default_rng(3)
     for dtype in INT_DTYPES:
         for op in OPS:
+            if not _defined(dtype, op):
+                continue
             for n in list(range(1, 17)) + [31, 64]:
                 x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
                 if op == "sum" and rng.random() < 0.5:
@@ -239,6 +250,8 @@ def pin_brute_force_exhaustive_tiny(orc):
     alphabet = [0, 1, 2, 0x7FFFFFFF, 0x80000000, 0xFFFFFFFF]
     for dtype in INT_DTYPES:
         for op in OPS:
+            if not _defined(dtype, op):
+                continue
             for n in range(1, 5):
                 for combo in itertools.product(alphabet, repeat=n):
                     x = np.array(combo, np.uint32)
@@ -246,6 +259,87 @@ def pin_brute_force_exhaustive_tiny(orc):
                     b = list(combo)
                     assert _bits(orc.scan(x, op, True).y) == brute.inclusive_bits(b, dtype, op)
                     assert _bits(orc.scan(x, op, False).y) == brute.exclusive_bits(b, dtype, op)
+
+
+def pin_more_operators_numpy(orc):
+    """min / and / or / product against numpy's own accumulations ([Blog2] 3.3)."""
+    rng = np.random.default_rng(29)
+    for n in (1, 2, 33, 1000):
+        xu = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+        xi = xu.view(np.int32)
+        assert np.array_equal(orc.scan(xu, "min", True).y, np.minimum.accumulate(xu))
+        assert np.array_equal(orc.scan(xi, "min", True).y, np.minimum.accumulate(xi))
+        assert np.array_equal(orc.scan(xu, "and", True).y, np.bitwise_and.accumulate(xu))
+        assert np.array_equal(orc.scan(xu, "or", True).y, np.bitwise_or.accumulate(xu))
+        assert np.array_equal(orc.scan(xu, "prod", True).y, np.multiply.accumulate(xu, dtype=np.uint32))
+        assert np.array_equal(orc.scan(xi, "prod", True).y.view(np.uint32),
+                              np.multiply.accumulate(xu, dtype=np.uint32))
+        xf = rng.standard_normal(n).astype(np.float32)
+        assert np.array_equal(orc.scan(xf, "min", True).y, np.minimum.accumulate(xf))
+
+
+def pin_more_operators_closed_forms(orc):
+    n = 200
+    i = np.arange(n)
+    desc = (1000 - i).astype(np.int32)
+    assert np.array_equal(orc.scan(desc, "min", True).y, desc)
+    assert np.all(orc.scan(desc[::-1].copy(), "min", True).y == desc[-1])
+    threes = np.full(n, 3, np.uint32)
+    assert _bits(orc.scan(threes, "prod", True).y) == [pow(3, k + 1, 1 << 32) for k in range(n)]
+    assert _bits(orc.scan(threes, "prod", False).y) == [pow(3, k, 1 << 32) for k in range(n)]
+    bit = np.array([1 << (k % 32) for k in range(n)], np.uint32)
+    assert _bits(orc.scan(bit, "or", True).y) == [(1 << min(k + 1, 32)) - 1 for k in range(n)]
+    clear = ~bit
+    assert _bits(orc.scan(clear, "and", True).y) == [M32 ^ ((1 << min(k + 1, 32)) - 1)
+                                                    for k in range(n)]
+    ones = np.full(n, (1 << 16) | 1, np.uint32)            # v -> v + 1
+    assert _bits(orc.scan(ones, "affine", True).y) == [(1 << 16) | ((k + 1) & 0xFFFF)
+                                                      for k in range(n)]
+    tri = np.full(n, 3 << 16, np.uint32)                   # v -> 3 v
+    assert _bits(orc.scan(tri, "affine", True).y) == [pow(3, k + 1, 1 << 16) << 16 for k in range(n)]
+    # float min: the right-most of equal minima, and the +inf identity
+    f = np.array([0.0, -0.0, 1.0, -0.0, 0.0], np.float32)
+    assert _bits(orc.scan(f, "min", True).y) == _bits(np.array([0.0, -0.0, -0.0, -0.0, 0.0],
+                                                               np.float32))
+    assert _bits(orc.scan(f, "min", False).y[:1]) == [0x7F800000]
+
+
+def pin_affine_maps_compose_in_order(orc):
+    """Scanning affine maps ([Scan3] 三: a non-commutative operator keeps its left-right
+    order): y[i] applied to v equals applying x[0], x[1], ..., x[i] to v one after the
+    other, computed here by plain evaluation, without composing anything."""
+    rng = np.random.default_rng(31)
+    for n in (1, 2, 5, 64, 300):
+        x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+        y = _bits(orc.scan(x, "affine", True).y)
+        z = _bits(orc.scan(x, "affine", False).y)
+        for v0 in (0, 1, 12345, 65535):
+            v = v0
+            for k in range(n):
+                assert ((z[k] >> 16) * v0 + (z[k] & 0xFFFF)) & 0xFFFF == v
+                a, b = int(x[k]) >> 16, int(x[k]) & 0xFFFF
+                v = (a * v + b) & 0xFFFF
+                assert ((y[k] >> 16) * v0 + (y[k] & 0xFFFF)) & 0xFFFF == v
+
+
+def pin_float_product(orc):
+    """Products of powers of two are exact in any order; other products match the
+    exact rational product within the double's own rounding."""
+    import fractions
+    rng = np.random.default_rng(37)
+    p2 = np.ldexp(1.0, rng.integers(-3, 4, 100)).astype(np.float32) * rng.choice([-1, 1], 100)
+    want, acc = [], 1.0
+    for v in p2.tolist():
+        acc *= v
+        want.append(acc)
+    assert orc.scan(p2.astype(np.float32), "prod", True).y.tolist() == want
+    xs = rng.uniform(0.5, 2.0, 200).astype(np.float32)
+    y = orc.scan(xs, "prod", True).y
+    exact = fractions.Fraction(1)
+    for k, v in enumerate(xs.tolist()):
+        exact *= fractions.Fraction(v)
+        assert abs(fractions.Fraction(float(y[k])) - exact) <= exact * (k + 1) * fractions.Fraction(1, 2**52)
+    assert orc.scan(xs, "prod", False).y[0] == 1.0
 
 
 def pin_compaction_brute_and_numpy(orc):

@@ -20,8 +20,8 @@ MUTANTS = [
     ("xor_is_or", "return a ^ b;", "return a | b;"),
     ("max_identity_zero", "return dtype == OR_INT32 ? 0x80000000u : 0u;", "return 0u;"),
     ("int32_max_unsigned", "return ((int32_t)a > (int32_t)b) ? a : b;", "return (a > b) ? a : b;"),
-    ("uint32_max_signed", "        return (a > b) ? a : b;\n    }",
-     "        return ((int32_t)a > (int32_t)b) ? a : b;\n    }"),
+    ("uint32_max_signed", "        return (a > b) ? a : b;\n    case OR_MIN:",
+     "        return ((int32_t)a > (int32_t)b) ? a : b;\n    case OR_MIN:"),
     ("f32_sum_sign", "acc = (i == 0) ? v : acc + v;", "acc = (i == 0) ? v : acc - v;"),
     ("f32_exclusive_dropped_term", "            y[i] = acc;\n            acc += v;",
      "            y[i] = acc;\n            acc = v;"),
@@ -49,6 +49,19 @@ MUTANTS = [
      "        return k;\n    if (dtype == OR_FLOAT32)"),
     ("sort_float_negatives", "return (k & 0x80000000u) ? ~k : (k | 0x80000000u);",
      "return (k & 0x80000000u) ? (k ^ 0x80000000u) : (k | 0x80000000u);"),
+    ("min_identity_zero", "return dtype == OR_INT32 ? 0x7fffffffu : 0xffffffffu; /* largest value */",
+     "return 0u;"),
+    ("int32_min_unsigned", "            return ((int32_t)a < (int32_t)b) ? a : b;",
+     "            return (a < b) ? a : b;"),
+    ("and_identity_zero", "    case OR_AND:\n        return 0xffffffffu;", "    case OR_AND:\n        return 0u;"),
+    ("prod_identity_zero", "    case OR_PROD:\n        return 1u;", "    case OR_PROD:\n        return 0u;"),
+    ("or_is_xor", "        return a | b;", "        return a ^ b;"),
+    ("affine_order_swapped", "        return affine_then(a, b);", "        return affine_then(b, a);"),
+    ("affine_offset_term", "uint32_t b = (a2 * b1 + b2) & 0xffffu;", "uint32_t b = (a1 * b2 + b1) & 0xffffu;"),
+    ("f32_min_tie_left", "    return (a < b) ? a : b;\n}\n\nvoid oracle_scan_f32_min",
+     "    return (a <= b) ? a : b;\n}\n\nvoid oracle_scan_f32_min"),
+    ("f32_prod_exclusive_dropped_term", "            y[i] = acc;\n            acc *= v;",
+     "            acc *= v;\n            y[i] = acc;"),
 ]
 
 
