@@ -42,12 +42,12 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 1
+#define LS_ABI_VERSION 2
 
 typedef enum ls_status {
     LS_OK = 0,
     LS_ERR_INVALID_ARG = 1, /* bad size, NULL, alignment, enum value, or overlap */
-    LS_ERR_UNSUPPORTED = 2, /* a valid combination the library does not define (float32 xor) */
+    LS_ERR_UNSUPPORTED = 2, /* an operator not defined for the element type (see ls_op) */
     LS_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the size query returned */
     LS_ERR_HIP = 4          /* the HIP runtime reported an error when enqueuing */
 } ls_status;
@@ -55,18 +55,41 @@ typedef enum ls_status {
 /* Element types.  All are 32 bits wide. */
 typedef enum ls_dtype { LS_INT32 = 0, LS_UINT32 = 1, LS_FLOAT32 = 2 } ls_dtype;
 
-/* Associative operators ([Scan3] 一 and 三; [Blog2] 3.3).
- *   LS_SUM  int32/uint32: addition modulo 2^32 (two's complement wrap);
- *           float32: IEEE addition; association order is the library's, so
- *           results may differ from a serial sum in the last bits ([Scan3]
- *           pitfall list) and may differ between runs.
- *   LS_MAX  int32 signed, uint32 unsigned, float32 (a > b) ? a : b, which on a
- *           tie keeps the later element; bit-exact and run-to-run identical for
- *           data without NaN.  NaN inputs give unspecified results.
- *   LS_XOR  int32/uint32 bitwise; float32 -> LS_ERR_UNSUPPORTED.
- * Identity (first exclusive cell, value for n = 0): 0 for sum and xor
- * (+0.0f for float32), INT32_MIN / 0u / -infinity for max. */
-typedef enum ls_op { LS_SUM = 0, LS_MAX = 1, LS_XOR = 2 } ls_op;
+/* Associative operators ([Scan3] 一 and 三; [Blog2] 3.3), combined as
+ * op(earlier, later), left to right.
+ *   LS_SUM     int32/uint32: addition modulo 2^32 (two's complement wrap);
+ *              float32: IEEE addition; association order is the library's, so
+ *              results may differ from a serial sum in the last bits ([Scan3]
+ *              pitfall list) and, with the single pass, between runs.
+ *   LS_MAX     int32 signed, uint32 unsigned, float32 (a > b) ? a : b, which on a
+ *              tie keeps the later element; bit-exact and run-to-run identical
+ *              for data without NaN.  NaN inputs give unspecified results.
+ *   LS_XOR     int32/uint32 bitwise; float32 -> LS_ERR_UNSUPPORTED.
+ *   LS_MIN     as LS_MAX with (a < b) ? a : b (ties keep the later element).
+ *   LS_AND, LS_OR  int32/uint32 bitwise ([Blog2] 3.3: logical AND/OR);
+ *              float32 -> LS_ERR_UNSUPPORTED.
+ *   LS_PROD    int32/uint32: multiplication modulo 2^32; float32: IEEE product
+ *              (relative error up to about (i+1) * 2^-24 at element i, any
+ *              association; [Blog2] 3.3).
+ *   LS_AFFINE  uint32 only: element (a << 16) | b is the map v -> a*v + b mod
+ *              2^16 (the 2x2 matrix [[a, b], [0, 1]]); the scan composes the maps,
+ *              earlier applied first.  Not commutative, so it shows that results
+ *              keep their left-right order ([Scan3] 三, matrix chain products).
+ *              int32/float32 -> LS_ERR_UNSUPPORTED.
+ * Identity (first exclusive cell, value for n = 0): 0 for sum, xor and or
+ * (+0.0f for float32); INT32_MIN / 0u / -infinity for max; INT32_MAX /
+ * 0xFFFFFFFF / +infinity for min; all ones for and; 1 (1.0f) for prod; the
+ * identity map 0x00010000 for affine. */
+typedef enum ls_op {
+    LS_SUM = 0,
+    LS_MAX = 1,
+    LS_XOR = 2,
+    LS_MIN = 3,
+    LS_AND = 4,
+    LS_OR = 5,
+    LS_PROD = 6,
+    LS_AFFINE = 7
+} ls_op;
 
 /* Compaction predicates: keep x when (x CMP threshold), compared in the element
  * type (signed, unsigned, or IEEE float with C semantics: NaN satisfies only NE). */
@@ -118,7 +141,7 @@ const char *ls_status_string(ls_status s);
 /* Workspace size for scan_inclusive / scan_exclusive.
  *   bytes (host, out): size of the device workspace a call with these arguments
  *   needs (never 0).  Errors: LS_ERR_INVALID_ARG for n < 0, bytes == NULL or an
- *   unknown enum; LS_ERR_UNSUPPORTED for float32 xor. */
+ *   unknown enum; LS_ERR_UNSUPPORTED for an operator not defined on t (see ls_op). */
 ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t *bytes);
 
 /* Inclusive scan: out[i] = in[0] (+) in[1] (+) ... (+) in[i].     [Scan3] 一

@@ -31,7 +31,7 @@ _LIB_PATH = os.path.join(_PKG, "libscan.so")
 
 LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = range(5)
 DTYPE_CODES = {"int32": 0, "uint32": 1, "float32": 2}
-OP_CODES = {"sum": 0, "max": 1, "xor": 2}
+OP_CODES = {"sum": 0, "max": 1, "xor": 2, "min": 3, "and": 4, "or": 5, "prod": 6, "affine": 7}
 CMP_CODES = {"lt": 0, "le": 1, "gt": 2, "ge": 3, "eq": 4, "ne": 5}
 SCHEME_CODES = {"single_pass": 0, "reduce_then_scan": 1, "scan_then_propagate": 2}
 BLOCK_SCAN_CODES = {"wave_dpp": 0, "hillis_steele": 1, "hillis_steele_double": 2, "blelloch": 3}
@@ -41,6 +41,7 @@ if hasattr(torch, "uint32"):
 
 _lock = threading.Lock()
 _lib = None
+ABI_VERSION = 2  # the libscan.h version this binding marshals for
 
 
 class LibscanError(RuntimeError):
@@ -69,6 +70,9 @@ def load_library():
                               ctypes.c_size_t)
         lib.ls_abi_version.argtypes = []
         lib.ls_abi_version.restype = I
+        if lib.ls_abi_version() != ABI_VERSION:
+            raise ImportError(f"{_LIB_PATH} has ABI version {lib.ls_abi_version()}, this binding "
+                              f"needs {ABI_VERSION}; rebuild with `python -m prefix_scan_stream_amd.build`")
         lib.ls_status_string.argtypes = [I]
         lib.ls_status_string.restype = ctypes.c_char_p
         lib.ls_scan_workspace_bytes.argtypes = [I64, I, I, ctypes.POINTER(SZ)]

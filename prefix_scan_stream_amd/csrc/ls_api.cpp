@@ -12,7 +12,15 @@
 namespace {
 
 bool valid_dtype(ls_dtype t) { return t == LS_INT32 || t == LS_UINT32 || t == LS_FLOAT32; }
-bool valid_op(ls_op op) { return op == LS_SUM || op == LS_MAX || op == LS_XOR; }
+bool valid_op(ls_op op) { return op >= LS_SUM && op <= LS_AFFINE; }
+// Valid (dtype, op) pairs the library does not define: bitwise operators and
+// affine maps on float32, affine maps on int32.
+bool op_unsupported(ls_dtype t, ls_op op)
+{
+    if (t == LS_FLOAT32)
+        return op == LS_XOR || op == LS_AND || op == LS_OR || op == LS_AFFINE;
+    return op == LS_AFFINE && t != LS_UINT32;
+}
 bool valid_cmp(ls_cmp c) { return c >= LS_LT && c <= LS_NE; }
 bool valid_scheme(ls_scheme c) { return c >= LS_SCHEME_SINGLE_PASS && c <= LS_SCHEME_SCAN_THEN_PROPAGATE; }
 bool valid_block_scan(ls_block_scan c) { return c >= LS_BLOCK_WAVE_DPP && c <= LS_BLOCK_BLELLOCH; }
@@ -56,7 +64,7 @@ ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op
         if (!aligned(total, 4) || overlaps(total, 4, in, bytes) || overlaps(total, 4, out, bytes))
             return LS_ERR_INVALID_ARG;
     }
-    if (t == LS_FLOAT32 && op == LS_XOR)
+    if (op_unsupported(t, op))
         return LS_ERR_UNSUPPORTED;
     const size_t need = ls::scan_workspace_bytes(n, int(scheme));
     ls_status st = check_ws(ws, ws_bytes, need);
@@ -129,7 +137,7 @@ ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t* bytes
 {
     if (bytes == nullptr || !size_ok(n) || !valid_dtype(t) || !valid_op(op))
         return LS_ERR_INVALID_ARG;
-    if (t == LS_FLOAT32 && op == LS_XOR)
+    if (op_unsupported(t, op))
         return LS_ERR_UNSUPPORTED;
     *bytes = ls::scan_workspace_bytes(n, ls::SCHEME_SINGLE_PASS);
     return LS_OK;
@@ -139,7 +147,7 @@ ls_status ls_scan_ex_workspace_bytes(int64_t n, ls_dtype t, ls_op op, ls_scheme 
 {
     if (bytes == nullptr || !size_ok(n) || !valid_dtype(t) || !valid_op(op) || !valid_scheme(scheme))
         return LS_ERR_INVALID_ARG;
-    if (t == LS_FLOAT32 && op == LS_XOR)
+    if (op_unsupported(t, op))
         return LS_ERR_UNSUPPORTED;
     *bytes = ls::scan_workspace_bytes(n, int(scheme));
     return LS_OK;
@@ -212,7 +220,7 @@ static ls_status batched_common(const void* in, void* out, int64_t rows, int64_t
         if (in != out && overlaps(in, bytes, out, bytes))
             return LS_ERR_INVALID_ARG;
     }
-    if (t == LS_FLOAT32 && op == LS_XOR)
+    if (op_unsupported(t, op))
         return LS_ERR_UNSUPPORTED;
     return from_hip(ls::launch_batched(in, out, rows, cols, int(t), int(op), exclusive != 0, int(kind),
                                        reinterpret_cast<hipStream_t>(stream)));

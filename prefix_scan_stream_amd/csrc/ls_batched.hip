@@ -338,6 +338,22 @@ hipError_t launch_batched(const void* in, void* out, int64_t rows, int64_t cols,
         if (dtype == DT_UINT32)
             return run_batched<MaxU32>(in, out, rows, cols, excl, kind, s);
         return run_batched<MaxF32>(in, out, rows, cols, excl, kind, s);
+    case OP_MIN:
+        if (dtype == DT_INT32)
+            return run_batched<MinI32>(in, out, rows, cols, excl, kind, s);
+        if (dtype == DT_UINT32)
+            return run_batched<MinU32>(in, out, rows, cols, excl, kind, s);
+        return run_batched<MinF32>(in, out, rows, cols, excl, kind, s);
+    case OP_AND:
+        return run_batched<AndU32>(in, out, rows, cols, excl, kind, s);
+    case OP_OR:
+        return run_batched<OrU32>(in, out, rows, cols, excl, kind, s);
+    case OP_PROD:
+        if (dtype == DT_FLOAT32)
+            return run_batched<MulF32>(in, out, rows, cols, excl, kind, s);
+        return run_batched<MulU32>(in, out, rows, cols, excl, kind, s);
+    case OP_AFFINE:
+        return run_batched<AffU32>(in, out, rows, cols, excl, kind, s);
     }
     return hipErrorInvalidValue;
 }

@@ -23,38 +23,105 @@ namespace ls {
 
 // ---------------------------------------------------------------- operators
 // Every combine in the library is written apply(earlier, later).  For the float
-// max that order matters on ties (the later element wins), and keeping it
+// max and min that order matters on ties (the later element wins), and keeping it
 // everywhere makes the result independent of how the work is split.
+// `commutative` says whether apply(a, b) and apply(b, a) give the same bits; a
+// reduction may regroup elements out of order only when it does (float sums and
+// products are commutative, if not associative).
 
 struct SumU32 {
     using T = uint32_t;
+    static constexpr bool commutative = true;
     static __device__ __forceinline__ T identity() { return 0u; }
     static __device__ __forceinline__ T apply(T a, T b) { return a + b; }
 };
 struct XorU32 {
     using T = uint32_t;
+    static constexpr bool commutative = true;
     static __device__ __forceinline__ T identity() { return 0u; }
     static __device__ __forceinline__ T apply(T a, T b) { return a ^ b; }
 };
 struct MaxU32 {
     using T = uint32_t;
+    static constexpr bool commutative = true;
     static __device__ __forceinline__ T identity() { return 0u; }
     static __device__ __forceinline__ T apply(T a, T b) { return a > b ? a : b; }
 };
 struct MaxI32 {
     using T = int32_t;
+    static constexpr bool commutative = true;
     static __device__ __forceinline__ T identity() { return INT32_MIN; }
     static __device__ __forceinline__ T apply(T a, T b) { return a > b ? a : b; }
 };
 struct SumF32 {
     using T = float;
+    static constexpr bool commutative = true;
     static __device__ __forceinline__ T identity() { return 0.0f; }
     static __device__ __forceinline__ T apply(T a, T b) { return a + b; }
 };
 struct MaxF32 {
     using T = float;
+    static constexpr bool commutative = false;
     static __device__ __forceinline__ T identity() { return -__builtin_inff(); }
     static __device__ __forceinline__ T apply(T a, T b) { return a > b ? a : b; }
+};
+// min keeps the later element on ties, like max.
+struct MinU32 {
+    using T = uint32_t;
+    static constexpr bool commutative = true;
+    static __device__ __forceinline__ T identity() { return 0xffffffffu; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a < b ? a : b; }
+};
+struct MinI32 {
+    using T = int32_t;
+    static constexpr bool commutative = true;
+    static __device__ __forceinline__ T identity() { return INT32_MAX; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a < b ? a : b; }
+};
+struct MinF32 {
+    using T = float;
+    static constexpr bool commutative = false;
+    static __device__ __forceinline__ T identity() { return __builtin_inff(); }
+    static __device__ __forceinline__ T apply(T a, T b) { return a < b ? a : b; }
+};
+struct AndU32 {
+    using T = uint32_t;
+    static constexpr bool commutative = true;
+    static __device__ __forceinline__ T identity() { return 0xffffffffu; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a & b; }
+};
+struct OrU32 {
+    using T = uint32_t;
+    static constexpr bool commutative = true;
+    static __device__ __forceinline__ T identity() { return 0u; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a | b; }
+};
+// Product: wraps modulo 2^32 for int32 and uint32 (same low bits).
+struct MulU32 {
+    using T = uint32_t;
+    static constexpr bool commutative = true;
+    static __device__ __forceinline__ T identity() { return 1u; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a * b; }
+};
+struct MulF32 {
+    using T = float;
+    static constexpr bool commutative = true;
+    static __device__ __forceinline__ T identity() { return 1.0f; }
+    static __device__ __forceinline__ T apply(T a, T b) { return a * b; }
+};
+// Composition of affine maps v -> a v + b (mod 2^16), packed (a << 16) | b: the
+// 2x2 matrix [[a, b], [0, 1]].  The earlier map is applied first, so
+// apply(earlier, later) is the map v -> a2 (a1 v + b1) + b2.  Not commutative: a
+// scan under it checks that every combine keeps its left-right order.
+struct AffU32 {
+    using T = uint32_t;
+    static constexpr bool commutative = false;
+    static __device__ __forceinline__ T identity() { return 0x00010000u; }
+    static __device__ __forceinline__ T apply(T e, T l)
+    {
+        const uint32_t a1 = e >> 16, b1 = e & 0xffffu, a2 = l >> 16, b2 = l & 0xffffu;
+        return (((a2 * a1) & 0xffffu) << 16) | ((a2 * b1 + b2) & 0xffffu);
+    }
 };
 
 template <class T>
@@ -184,6 +251,14 @@ __device__ __forceinline__ Run4<T> load_run_x1(__amdgpu_buffer_rsrc_t rs, uint32
     return r;
 }
 
+// A store of more than 64 bits reads its data registers after it issues, so a
+// VALU write to those registers right behind it needs a wait state.  The
+// compiler inserts that wait only when the store's soffset operand is not a
+// register; with the run offset in an SGPR soffset it let the next instruction
+// overwrite the first data register, and gfx950 then stored the new value in
+// some tiles (measured: one element per run, varying from run to run).  So the
+// whole offset goes into voffset and soffset is the constant 0; tests/
+// test_codegen.py checks that no 128-bit buffer store takes a register soffset.
 template <class T>
 __device__ __forceinline__ void store_run_x4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
                                              const Run4<T>& r)
@@ -193,7 +268,7 @@ __device__ __forceinline__ void store_run_x4(__amdgpu_buffer_rsrc_t rs, uint32_t
     w.y = to_bits(r.v[1]);
     w.z = to_bits(r.v[2]);
     w.w = to_bits(r.v[3]);
-    __builtin_amdgcn_raw_buffer_store_b128(w, rs, voff, soff, STORE_POLICY);
+    __builtin_amdgcn_raw_buffer_store_b128(w, rs, voff + soff, 0, STORE_POLICY);
 }
 
 template <class T>
@@ -202,7 +277,7 @@ __device__ __forceinline__ void store_run_x1(__amdgpu_buffer_rsrc_t rs, uint32_t
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        __builtin_amdgcn_raw_buffer_store_b32(to_bits(r.v[k]), rs, voff + 4 * k, soff, STORE_POLICY);
+        __builtin_amdgcn_raw_buffer_store_b32(to_bits(r.v[k]), rs, voff + soff + 4 * k, 0, STORE_POLICY);  // see store_run_x4
 }
 
 // Element-wise global access with an explicit range check (row kernels).

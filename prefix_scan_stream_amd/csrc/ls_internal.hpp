@@ -10,7 +10,9 @@ namespace ls {
 
 // Element-type and operator codes (the values of ls_dtype / ls_op / ls_cmp).
 enum Dtype : int { DT_INT32 = 0, DT_UINT32 = 1, DT_FLOAT32 = 2 };
-enum OpCode : int { OP_SUM = 0, OP_MAX = 1, OP_XOR = 2 };
+enum OpCode : int {
+    OP_SUM = 0, OP_MAX = 1, OP_XOR = 2, OP_MIN = 3, OP_AND = 4, OP_OR = 5, OP_PROD = 6, OP_AFFINE = 7
+};
 // Device-wide schemes (the values of ls_scheme).
 enum Scheme : int { SCHEME_SINGLE_PASS = 0, SCHEME_REDUCE_THEN_SCAN = 1, SCHEME_SCAN_THEN_PROPAGATE = 2 };
 

@@ -187,26 +187,55 @@ __global__ __launch_bounds__(SCAN_BLOCK) void tile_reduce_kernel(const typename 
     const uint32_t valid = rem < SCAN_TILE ? uint32_t(rem) : uint32_t(SCAN_TILE);
     const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tile * SCAN_TILE, valid * 4u);
     const uint32_t voff = uint32_t(tid) * 16u;
-    T acc = Op::identity();
+    if constexpr (Op::commutative) {
+        // a thread folds its own runs (1024 elements apart), then the lanes and
+        // the waves: out of element order, which only a commutative op allows
+        T acc = Op::identity();
 #pragma unroll
-    for (int j = 0; j < SCAN_CHUNKS; ++j) {
-        const Run4<T> r = VEC ? load_run_x4<T>(rin, voff, j * SCAN_BLOCK * 16u)
-                              : load_run_x1<T>(rin, voff, j * SCAN_BLOCK * 16u);
-        const uint32_t e0 = 4u * uint32_t(j * SCAN_BLOCK + tid);
+        for (int j = 0; j < SCAN_CHUNKS; ++j) {
+            const Run4<T> r = VEC ? load_run_x4<T>(rin, voff, j * SCAN_BLOCK * 16u)
+                                  : load_run_x1<T>(rin, voff, j * SCAN_BLOCK * 16u);
+            const uint32_t e0 = 4u * uint32_t(j * SCAN_BLOCK + tid);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            acc = Op::apply(acc, e0 + k < valid ? r.v[k] : Op::identity());
-    }
-    const T inc = wave_inclusive_scan<Op>(acc);
-    if (lane == 63)
-        s_w[wave] = inc;
-    __syncthreads();
-    if (tid == 0) {
-        T t = Op::identity();
+            for (int k = 0; k < 4; ++k)
+                acc = Op::apply(acc, e0 + k < valid ? r.v[k] : Op::identity());
+        }
+        const T inc = wave_inclusive_scan<Op>(acc);
+        if (lane == 63)
+            s_w[wave] = inc;
+        __syncthreads();
+        if (tid == 0) {
+            T t = Op::identity();
 #pragma unroll
-        for (int w = 0; w < SCAN_WAVES; ++w)
-            t = Op::apply(t, s_w[w]);
-        totals[tile] = t;
+            for (int w = 0; w < SCAN_WAVES; ++w)
+                t = Op::apply(t, s_w[w]);
+            totals[tile] = t;
+        }
+    } else {
+        // element order: each run of 4, the runs of one chunk across the wave in
+        // lane order, the (chunk, wave) parts chunk by chunk
+        __shared__ T s_p[SCAN_CHUNKS * SCAN_WAVES];
+#pragma unroll
+        for (int j = 0; j < SCAN_CHUNKS; ++j) {
+            const Run4<T> r = VEC ? load_run_x4<T>(rin, voff, j * SCAN_BLOCK * 16u)
+                                  : load_run_x1<T>(rin, voff, j * SCAN_BLOCK * 16u);
+            const uint32_t e0 = 4u * uint32_t(j * SCAN_BLOCK + tid);
+            T run = Op::identity();
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                run = Op::apply(run, e0 + k < valid ? r.v[k] : Op::identity());
+            const T inc = wave_inclusive_scan<Op>(run);
+            if (lane == 63)
+                s_p[j * SCAN_WAVES + wave] = inc;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            constexpr int PARTS = SCAN_CHUNKS * SCAN_WAVES;
+            static_assert(PARTS <= 64, "one wave combines the parts");
+            const T inc = wave_inclusive_scan<Op>(lane < PARTS ? s_p[lane] : Op::identity());
+            if (lane == 63)
+                totals[tile] = inc;
+        }
     }
 }
 
@@ -385,6 +414,14 @@ template <> uint32_t identity_bits<MaxU32>() { return 0u; }
 template <> uint32_t identity_bits<MaxI32>() { return 0x80000000u; }
 template <> uint32_t identity_bits<SumF32>() { return 0u; }
 template <> uint32_t identity_bits<MaxF32>() { return 0xff800000u; }
+template <> uint32_t identity_bits<MinU32>() { return 0xffffffffu; }
+template <> uint32_t identity_bits<MinI32>() { return 0x7fffffffu; }
+template <> uint32_t identity_bits<MinF32>() { return 0x7f800000u; }
+template <> uint32_t identity_bits<AndU32>() { return 0xffffffffu; }
+template <> uint32_t identity_bits<OrU32>() { return 0u; }
+template <> uint32_t identity_bits<MulU32>() { return 1u; }
+template <> uint32_t identity_bits<MulF32>() { return 0x3f800000u; }
+template <> uint32_t identity_bits<AffU32>() { return 0x00010000u; }
 
 template <class Op, int CHUNKS>
 static void launch_single_pass(const void* in, void* out, int64_t n, int64_t tiles, bool inclusive,
@@ -533,6 +570,22 @@ hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, 
         if (dtype == DT_UINT32)
             return run_scan_scheme<MaxU32>(in, out, n, inclusive, total, ws, scheme, s);
         return run_scan_scheme<MaxF32>(in, out, n, inclusive, total, ws, scheme, s);
+    case OP_MIN:
+        if (dtype == DT_INT32)
+            return run_scan_scheme<MinI32>(in, out, n, inclusive, total, ws, scheme, s);
+        if (dtype == DT_UINT32)
+            return run_scan_scheme<MinU32>(in, out, n, inclusive, total, ws, scheme, s);
+        return run_scan_scheme<MinF32>(in, out, n, inclusive, total, ws, scheme, s);
+    case OP_AND:
+        return run_scan_scheme<AndU32>(in, out, n, inclusive, total, ws, scheme, s);
+    case OP_OR:
+        return run_scan_scheme<OrU32>(in, out, n, inclusive, total, ws, scheme, s);
+    case OP_PROD:
+        if (dtype == DT_FLOAT32)
+            return run_scan_scheme<MulF32>(in, out, n, inclusive, total, ws, scheme, s);
+        return run_scan_scheme<MulU32>(in, out, n, inclusive, total, ws, scheme, s);
+    case OP_AFFINE:
+        return run_scan_scheme<AffU32>(in, out, n, inclusive, total, ws, scheme, s);
     }
     return hipErrorInvalidValue;
 }

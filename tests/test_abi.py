@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "libscan.h")
 
 INV, UNS, WS = ps.LS_ERR_INVALID_ARG, ps.LS_ERR_UNSUPPORTED, ps.LS_ERR_WORKSPACE
 INT32, UINT32, F32 = 0, 1, 2
-SUM, MAX, XOR = 0, 1, 2
+SUM, MAX, XOR, MIN, AND, OR, PROD, AFFINE = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @pytest.fixture(scope="module")
@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ps.ls_abi_version() == 1
+    assert ps.ls_abi_version() == 2
     for s in range(5):
         assert ps.ls_status_string(s).startswith("LS_")
     assert "unknown" in ps.ls_status_string(99)
@@ -95,8 +95,14 @@ def test_scan_validation(lib, fn):
     assert _scan(lib, fn, A_IN, A_OUT + 1, 10) == INV
     assert _scan(lib, fn, A_IN, A_IN + 4, 10) == INV                   # partial overlap
     assert _scan(lib, fn, A_IN, A_OUT, 10, t=3) == INV                 # bad dtype
-    assert _scan(lib, fn, A_IN, A_OUT, 10, op=5) == INV                # bad op
+    assert _scan(lib, fn, A_IN, A_OUT, 10, op=8) == INV                # bad op
+    assert _scan(lib, fn, A_IN, A_OUT, 10, op=-1) == INV
     assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=XOR) == UNS       # float xor
+    for op in (AND, OR, AFFINE):                                        # other bitwise / maps on floats
+        assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=op) == UNS
+    assert _scan(lib, fn, A_IN, A_OUT, 10, t=INT32, op=AFFINE) == UNS  # affine maps are uint32
+    for t, op in ((F32, MIN), (F32, PROD), (INT32, PROD), (UINT32, AFFINE), (INT32, AND)):
+        assert _scan(lib, fn, A_IN, A_OUT, 10, t=t, op=op, ws=None) == WS  # defined: reaches the ws check
     assert _scan(lib, fn, A_IN, A_OUT, 10, ws=None) == WS              # no workspace
     assert _scan(lib, fn, A_IN, A_OUT, 1 << 20, wsb=64) == WS          # workspace too small
     assert _scan(lib, fn, A_IN, A_OUT, 10, ws=A_WS + 8) == INV         # workspace misaligned
@@ -217,6 +223,9 @@ def test_batched_validation(lib):
     assert call(inp=None) == INV
     assert call(out=A_IN + 4) == INV
     assert call(t=F32, op=XOR) == UNS
+    assert call(t=F32, op=AFFINE) == UNS
+    assert call(t=INT32, op=AFFINE) == UNS
+    assert call(op=8) == INV
     assert call(rows=1 << 40, cols=1 << 40) == INV  # size overflow
     # empty shapes are a no-op even with NULL pointers (nothing is enqueued)
     assert call(inp=None, out=None, rows=0) == ps.LS_OK

@@ -83,3 +83,34 @@ def test_aligned_tiles_load_128_bits(asm, src, prefix):
     body = kernel_body(asm[src], prefix)
     assert len(re.findall(r"buffer_load_dwordx4", body)) >= 16
     assert not re.search(r"buffer_load_dword\s", body)
+
+
+def _vregs(spec):
+    m = re.match(r"v\[(\d+):(\d+)\]", spec)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", spec)
+    return {int(m.group(1))} if m else set()
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_wide_stores_keep_their_data_wait_state(asm, src):
+    """A store of more than 64 bits reads its data registers after it issues; a VALU
+    write to them right behind it needs one wait state.  The compiler inserts it
+    only when a buffer store's soffset is not a register, so no 96/128-bit buffer
+    store may take a register soffset, and no VALU may overwrite a wide store's data
+    as the very next instruction (that race stored wrong values on gfx950)."""
+    text = asm[src]
+    assert not re.search(r"buffer_store_dwordx[34] v\[\d+:\d+\], v\d+, s\[\d+:\d+\], s\d+", text)
+    ins = [l.strip() for l in text.split("\n")]
+    ins = [l for l in ins if l and not l.startswith((".", ";")) and not l.endswith(":")]
+    for k, line in enumerate(ins[:-1]):
+        m = re.match(r"(buffer|global)_store_dwordx[34]\s", line)
+        if not m:
+            continue
+        ops = [p.strip() for p in line.split(None, 1)[1].split(",")]
+        data = _vregs(ops[1] if m.group(1) == "global" else ops[0])
+        nxt = ins[k + 1]
+        if nxt.startswith("v_"):
+            dst = nxt.split(None, 1)[1].split(",")[0].strip()
+            assert not (_vregs(dst) & data), f"{src}: '{line}' then '{nxt}'"

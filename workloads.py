@@ -116,18 +116,37 @@ def rows1024(rows=None, cols=1024):
 
 def case(dtype: str, op: str, n: int, seed: int) -> np.ndarray:
     """A generic parity case: values chosen so each (dtype, op) is exercised
-    over its interesting range (sums small enough to stay meaningful, max over
-    signed/unsigned ranges, xor over full bit patterns)."""
+    over its interesting range (sums small enough to stay meaningful, max / min
+    over signed/unsigned ranges, xor over full bit patterns, and / or that change
+    at scattered places, odd factors for products and affine multipliers)."""
     if dtype == "float32":
         if op == "sum":
             return f32_uniform(n, -1.0, 1.0, seed)
+        if op == "prod":
+            # factors near +-1 keep long products finite and away from zero
+            g = rng(seed)
+            return (g.uniform(0.995, 1.005, n) * g.choice([-1.0, 1.0], n)).astype(np.float32)
         g = rng(seed)
         return (g.standard_normal(n) * 1e3).astype(np.float32)
+    if op in ("and", "or"):
+        # all ones (and) / all zeros (or) except a few words that clear / set one bit,
+        # so the prefix changes at scattered places instead of collapsing at once
+        g = rng(seed)
+        x = np.full(n, 0xFFFFFFFF if op == "and" else 0, np.uint32)
+        pos = g.choice(n, min(n, 64), replace=False) if n else np.zeros(0, np.int64)
+        b = (np.uint32(1) << g.integers(0, 32, pos.size).astype(np.uint32)).astype(np.uint32)
+        x[pos] = ~b if op == "and" else b
+        return x.view(np.int32) if dtype == "int32" else x
+    if op == "prod":
+        x = u32_bits(n, seed) | np.uint32(1)  # odd factors: units mod 2^32, never 0
+        return x.view(np.int32) if dtype == "int32" else x
+    if op == "affine":
+        return u32_bits(n, seed) | np.uint32(1 << 16)  # odd multipliers keep every map invertible
     if op == "sum":
         if dtype == "int32":
             return int_uniform(n, -1000, 1000, seed)
         return int_uniform(n, 0, 1 << 32, seed, dtype=np.uint32)
-    if op == "max":
+    if op in ("max", "min"):
         if dtype == "int32":
             return int_uniform(n, -(1 << 31), 1 << 31, seed, dtype=np.int32)
         return u32_bits(n, seed)
