@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
 ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
-            "blockscans", "sort", "select")
+            "blockscans", "sort", "select", "ops")
 DEFAULT_LEGS = ALL_LEGS
 
 
@@ -189,6 +189,9 @@ def main():
         n = wl.SIZES["fp32_scan"]
         xs = rotating(lambda i: to_dev(wl.fp32_scan()))
         bw_leg("fp32_sum_incl_2e26", xs, lambda a, b: ps.scan_inclusive(a, "sum", out=b), n, 8 * n)
+        # the fixed-order single pass: the same bits on every run
+        bw_leg("fp32_sum_incl_2e26_deterministic", xs,
+               lambda a, b: ps.scan_ex(a, "sum", True, "deterministic", out=b), n, 8 * n)
         del xs
     if "max" in legs:
         n = wl.SIZES["max_scan"]
@@ -225,6 +228,15 @@ def main():
         bw_leg("select_indices_if_i32_2e27_sel50", xs,
                lambda a, b: ps.select_indices_if(a, "lt", thr, out=b, count=cnt), n, 4 * n + 4 * kept)
         del xs, xh, fh, fd
+    if "ops" in legs:
+        # the further operators, inclusive scans of 2^26 elements
+        n = wl.SIZES["fp32_scan"]
+        for dt, op in (("int32", "min"), ("uint32", "or"), ("int32", "prod"), ("float32", "prod"),
+                       ("uint32", "affine")):
+            xs = rotating(lambda i, dt=dt, op=op: to_dev(wl.case(dt, op, n, seed=500 + i)))
+            bw_leg(f"{dt}_{op}_incl_2e26", xs, lambda a, b, op=op: ps.scan_inclusive(a, op, out=b),
+                   n, 8 * n)
+            del xs
     if "rows64" in legs:
         xs = rotating(lambda i: to_dev(wl.rows64()))
         n = xs[0].numel()

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 2
+#define LS_ABI_VERSION 3
 
 typedef enum ls_status {
     LS_OK = 0,
@@ -106,12 +106,23 @@ typedef enum ls_cmp { LS_LT = 0, LS_LE = 1, LS_GT = 2, LS_GE = 3, LS_EQ = 4, LS_
  *   LS_SCHEME_SCAN_THEN_PROPAGATE  tile scans with totals, a scan of the totals, an
  *                                  offset pass over the output: 4*n*4 bytes
  *                                  ([Scan3] 四, the three kernels as listed there).
+ *   LS_SCHEME_SINGLE_PASS_DETERMINISTIC  the single pass with a fixed order of
+ *                                  combination: tiles form groups of 64, the last
+ *                                  tile of a group publishes a full prefix, and a
+ *                                  tile combines it with its group's earlier totals
+ *                                  in a fixed order.  Float sums and products are
+ *                                  then the same bits on every run ([Scan3]
+ *                                  pitfall list: a reproducible float result needs
+ *                                  a fixed order).  Moves 2*n*4 bytes.
  * The three-phase schemes scan the tile totals recursively when they exceed one
- * tile, as [Scan3] 四 describes for very large arrays. */
+ * tile, as [Scan3] 四 describes for very large arrays.  Their order of combination
+ * depends only on n, so they too give the same bits on every run; only
+ * LS_SCHEME_SINGLE_PASS combines float values in an order that may vary. */
 typedef enum ls_scheme {
     LS_SCHEME_SINGLE_PASS = 0,
     LS_SCHEME_REDUCE_THEN_SCAN = 1,
-    LS_SCHEME_SCAN_THEN_PROPAGATE = 2
+    LS_SCHEME_SCAN_THEN_PROPAGATE = 2,
+    LS_SCHEME_SINGLE_PASS_DETERMINISTIC = 3
 } ls_scheme;
 
 /* Block-level scan used by batched_row_scan_ex for rows of more than 64 elements

@@ -33,7 +33,8 @@ LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = ra
 DTYPE_CODES = {"int32": 0, "uint32": 1, "float32": 2}
 OP_CODES = {"sum": 0, "max": 1, "xor": 2, "min": 3, "and": 4, "or": 5, "prod": 6, "affine": 7}
 CMP_CODES = {"lt": 0, "le": 1, "gt": 2, "ge": 3, "eq": 4, "ne": 5}
-SCHEME_CODES = {"single_pass": 0, "reduce_then_scan": 1, "scan_then_propagate": 2}
+SCHEME_CODES = {"single_pass": 0, "reduce_then_scan": 1, "scan_then_propagate": 2,
+                "deterministic": 3}
 BLOCK_SCAN_CODES = {"wave_dpp": 0, "hillis_steele": 1, "hillis_steele_double": 2, "blelloch": 3}
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "float32"}
 if hasattr(torch, "uint32"):
@@ -41,7 +42,7 @@ if hasattr(torch, "uint32"):
 
 _lock = threading.Lock()
 _lib = None
-ABI_VERSION = 2  # the libscan.h version this binding marshals for
+ABI_VERSION = 3  # the libscan.h version this binding marshals for
 
 
 class LibscanError(RuntimeError):

@@ -22,7 +22,7 @@ bool op_unsupported(ls_dtype t, ls_op op)
     return op == LS_AFFINE && t != LS_UINT32;
 }
 bool valid_cmp(ls_cmp c) { return c >= LS_LT && c <= LS_NE; }
-bool valid_scheme(ls_scheme c) { return c >= LS_SCHEME_SINGLE_PASS && c <= LS_SCHEME_SCAN_THEN_PROPAGATE; }
+bool valid_scheme(ls_scheme c) { return c >= LS_SCHEME_SINGLE_PASS && c <= LS_SCHEME_SINGLE_PASS_DETERMINISTIC; }
 bool valid_block_scan(ls_block_scan c) { return c >= LS_BLOCK_WAVE_DPP && c <= LS_BLOCK_BLELLOCH; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

@@ -487,4 +487,41 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
     }
 }
 
+// Fixed-association variant ([Scan3] pitfall list: float addition does not
+// associate, so a reproducible result needs a fixed order).  Tiles form groups
+// of LB_GROUP.  Only the last tile of a group publishes a full prefix; every
+// other tile publishes only its total.  Tile t's exclusive prefix is the full
+// prefix of the last tile of the previous group combined with the totals of the
+// earlier tiles of its own group, all in one wave in lane order (lane 0 the
+// prefix, lane l the total of the group's tile l - 1).  Which words are combined,
+// and how, depends only on t, never on timing, so the result is the same bits on
+// every run.  The price: a tile waits for exactly those words (no adaptive walk).
+constexpr int LB_GROUP = 64;
+
+template <class Codec>
+__device__ typename Codec::V lookback_grouped(const uint64_t* status, int64_t tile, WsHeader* hdr)
+{
+    using V = typename Codec::V;
+    const int lane = lane_id();
+    const int64_t g0 = tile - tile % LB_GROUP;  // first tile of this tile's group
+    const int before = int(tile - g0);         // tiles of the group before this one
+    const bool needed = lane == 0 ? g0 > 0 : lane <= before;
+    const int64_t idx = lane == 0 ? g0 - 1 : g0 + lane - 1;
+    int spins = 0;
+    for (;;) {
+        const uint64_t w = needed ? status_load(status + idx * STATUS_STRIDE)
+                                  : Codec::pack(ST_AGGREGATE, Codec::identity());
+        const uint32_t f = Codec::flag(w);
+        const bool ready = !needed || (lane == 0 ? f == ST_PREFIX : f != ST_EMPTY);
+        if (!__ballot(!ready))
+            return Codec::wave_reduce(needed ? Codec::value(w) : Codec::identity(), -1);
+        if (++spins >= LOOKBACK_SPIN_LIMIT) {
+            if (lane == 0)
+                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
+            return Codec::identity();  // only reached on a defect; the error word reports it
+        }
+        __builtin_amdgcn_s_sleep(LB_SLEEP);
+    }
+}
+
 }  // namespace ls

@@ -14,7 +14,10 @@ enum OpCode : int {
     OP_SUM = 0, OP_MAX = 1, OP_XOR = 2, OP_MIN = 3, OP_AND = 4, OP_OR = 5, OP_PROD = 6, OP_AFFINE = 7
 };
 // Device-wide schemes (the values of ls_scheme).
-enum Scheme : int { SCHEME_SINGLE_PASS = 0, SCHEME_REDUCE_THEN_SCAN = 1, SCHEME_SCAN_THEN_PROPAGATE = 2 };
+enum Scheme : int {
+    SCHEME_SINGLE_PASS = 0, SCHEME_REDUCE_THEN_SCAN = 1, SCHEME_SCAN_THEN_PROPAGATE = 2,
+    SCHEME_SINGLE_PASS_FIXED = 3
+};
 
 // ---- single-pass device-wide scan (ls_scan.hip)
 // Zeroes the workspace header and the status word of each of `tiles` tile slots.

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ps.ls_abi_version() == 2
+    assert ps.ls_abi_version() == ps.ABI_VERSION == 3
     for s in range(5):
         assert ps.ls_status_string(s).startswith("LS_")
     assert "unknown" in ps.ls_status_string(99)
@@ -116,10 +116,14 @@ def test_scan_validation(lib, fn):
 
 def test_extended_entry_points_validation(lib):
     sz = ctypes.c_size_t(0)
-    for scheme in range(3):
+    for scheme in range(4):
         assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, scheme, ctypes.byref(sz)) == 0
         assert sz.value > 0
-    assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, 3, ctypes.byref(sz)) == INV
+    single = ctypes.c_size_t(0)
+    lib.ls_scan_ex_workspace_bytes(1 << 20, F32, SUM, 0, ctypes.byref(single))
+    lib.ls_scan_ex_workspace_bytes(1 << 20, F32, SUM, 3, ctypes.byref(sz))
+    assert sz.value == single.value  # the deterministic single pass needs the same workspace
+    assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, 4, ctypes.byref(sz)) == INV
     assert lib.ls_scan_ex_workspace_bytes(10, F32, XOR, 1, ctypes.byref(sz)) == UNS
     # three-phase workspaces grow with the recursion over the tile totals
     assert ps.ls_scan_ex_workspace_bytes(1 << 34, "int32", "sum", "reduce_then_scan") > \
@@ -128,7 +132,8 @@ def test_extended_entry_points_validation(lib):
     def sx(scheme=0, n=10, ws=A_WS, wsb=BIG_WS, t=INT32, op=SUM, excl=1):
         return lib.scan_ex(A_IN, A_OUT, n, t, op, excl, scheme, None, ws, wsb, None)
 
-    assert sx(scheme=3) == INV
+    assert sx(scheme=4) == INV
+    assert sx(scheme=3, ws=None) == WS  # the deterministic single pass is a valid scheme
     assert sx(scheme=-1) == INV
     assert sx(scheme=1, n=-2) == INV
     assert sx(scheme=2, t=F32, op=XOR) == UNS

@@ -12,7 +12,7 @@ from gpu_util import DEV, bits, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 TILE = 16384  # the library tile; the sizes span tiles, ragged tails and many tiles
-SCHEMES = ["single_pass", "reduce_then_scan", "scan_then_propagate"]
+SCHEMES = ["single_pass", "reduce_then_scan", "scan_then_propagate", "deterministic"]
 COMBOS = [("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("uint32", "max"),
           ("float32", "sum"), ("float32", "max")]
 
@@ -64,3 +64,41 @@ def test_three_phase_recursive_totals(scheme):
 @pytest.mark.parametrize("scheme", SCHEMES)
 def test_scheme_big_scan_workload(scheme):
     check(wl.big_scan(), "sum", False, scheme)
+
+
+GROUP = 64  # tiles per group of the deterministic single pass
+
+
+@pytest.mark.parametrize("op", ["sum", "prod"])
+@pytest.mark.parametrize("n", [TILE * GROUP - 1, TILE * GROUP + 1, 3 * TILE * GROUP + 17,
+                               1 << 26])
+def test_deterministic_scheme_is_bitwise_reproducible(op, n):
+    """Float sums and products under the fixed-order single pass: within the
+    tolerance of the oracle, and the same bits on every one of several runs."""
+    x = wl.case("float32", op, n, seed=n + 11)
+    xd = to_dev(x)
+    first = None
+    for _ in range(4):
+        got = to_host(ps.scan_ex(xd, op, True, "deterministic"))
+        if first is None:
+            first = got.copy()
+            ref = oracle.scan(x, op, True)
+            if op == "sum":
+                ok, worst, k = oracle.fp32_sum_within_tolerance(got, ref)
+                assert ok, f"ratio {worst:.3g} at {k}"
+            else:
+                r = ref.y
+                k = np.arange(1, n + 1, dtype=np.float64)
+                assert np.all(np.abs(got - r) <= k * 2.0 ** -23 * np.abs(r) + 1e-30)
+        else:
+            assert np.array_equal(bits(got), bits(first)), "deterministic scan changed between runs"
+
+
+@pytest.mark.parametrize("n", [GROUP * TILE - 1, GROUP * TILE, GROUP * TILE + 1,
+                               2 * GROUP * TILE + TILE + 3, 300 * TILE + 5])
+def test_deterministic_scheme_keeps_order(n):
+    """Affine maps take the fixed-order kernel too: any combine out of order (the
+    group prefix on the wrong side, a total of the wrong tile) changes the bits."""
+    x = wl.case("uint32", "affine", n, seed=n + 13)
+    check(x, "affine", True, "deterministic")
+    check(x, "affine", False, "deterministic")
