@@ -76,6 +76,16 @@ def _bind(lib):
     lib.oracle_batched_f32_sum.restype = None
     lib.oracle_batched_f32_max.argtypes = [P, P, I64, I64, I]
     lib.oracle_batched_f32_max.restype = None
+    lib.oracle_segmented_u32.argtypes = [P, P, P, I64, I, I, I]
+    lib.oracle_segmented_u32.restype = I
+    lib.oracle_segmented_f32_sum.argtypes = [P, P, P, P, I64, I]
+    lib.oracle_segmented_f32_sum.restype = None
+    lib.oracle_segmented_f32_minmax.argtypes = [P, P, P, I64, I, I]
+    lib.oracle_segmented_f32_minmax.restype = None
+    lib.oracle_segmented_f32_prod.argtypes = [P, P, P, I64, I]
+    lib.oracle_segmented_f32_prod.restype = None
+    lib.oracle_heads_from_offsets.argtypes = [P, I64, P, I64]
+    lib.oracle_heads_from_offsets.restype = I
     lib.oracle_stable_sort.argtypes = [P, P, I64, I, P, P]
     lib.oracle_stable_sort.restype = I
     lib.oracle_sort_order_key.argtypes = [I, U32]
@@ -231,6 +241,48 @@ class Oracle:
         raise ValueError(f"oracle: op {op} is not defined for float32")
 
 
+    def segmented(self, x: np.ndarray, op: str = "sum", inclusive: bool = True,
+                  heads: np.ndarray | None = None, offsets: np.ndarray | None = None) -> ScanResult:
+        """Segmented scan of a 1-D array; segments by head flags (bytes, nonzero =
+        first element of a segment; element 0 always starts one) or by CSR offsets
+        (int64, offsets[0] = 0 ... offsets[-1] = n)."""
+        lib = self._lib
+        x = np.ascontiguousarray(x)
+        dt = _dtype_name(x)
+        n = x.shape[0]
+        if offsets is not None:
+            off = np.ascontiguousarray(offsets, dtype=np.int64)
+            h = np.zeros(max(n, 1), np.uint8)
+            if lib.oracle_heads_from_offsets(_ptr(off), off.shape[0] - 1, _ptr(h), n):
+                raise ValueError("oracle.segmented: offsets must run from 0 to n, non-decreasing")
+        else:
+            h = np.ascontiguousarray(heads, dtype=np.uint8)
+            if h.shape[0] != n:
+                raise ValueError("oracle.segmented: heads must have n bytes")
+            if n == 0:
+                h = np.zeros(1, np.uint8)
+        inc = 1 if inclusive else 0
+        if dt in ("int32", "uint32"):
+            y = np.empty(n, np.uint32)
+            if lib.oracle_segmented_u32(_ptr(x.view(np.uint32)), _ptr(y), _ptr(h), n, DTYPES[dt],
+                                        OPS[op], inc):
+                raise ValueError(f"oracle: bad op {op} for {dt}")
+            return ScanResult(y.view(x.dtype), None)
+        if op == "sum":
+            y = np.empty(n, np.float64)
+            b = np.empty(n, np.float64)
+            lib.oracle_segmented_f32_sum(_ptr(x), _ptr(y), _ptr(b), _ptr(h), n, inc)
+            return ScanResult(y, None, b)
+        if op in ("max", "min"):
+            y = np.empty(n, np.float32)
+            lib.oracle_segmented_f32_minmax(_ptr(x), _ptr(y), _ptr(h), n, inc, 1 if op == "min" else 0)
+            return ScanResult(y, None)
+        if op == "prod":
+            y = np.empty(n, np.float64)
+            lib.oracle_segmented_f32_prod(_ptr(x), _ptr(y), _ptr(h), n, inc)
+            return ScanResult(y, None)
+        raise ValueError(f"oracle: op {op} is not defined for float32")
+
     def sort(self, keys: np.ndarray, values: np.ndarray | None = None):
         """Stable ascending sort of 32-bit keys in their type's order (float32: IEEE
         total order); values, when given, follow their keys.  Returns (keys, values)."""
@@ -316,6 +368,10 @@ def compact_flags(x: np.ndarray, flags: np.ndarray):
 
 def indices(flags=None, x=None, cmp=None, threshold=None):
     return default().indices(flags, x, cmp, threshold)
+
+
+def segmented(x, op="sum", inclusive=True, heads=None, offsets=None):
+    return default().segmented(x, op, inclusive, heads, offsets)
 
 
 def fp32_sum_within_tolerance(got: np.ndarray, ref: ScanResult, rel: float = 1e-6,

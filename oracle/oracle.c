@@ -383,6 +383,119 @@ void oracle_batched_f32_prod(const float *x, double *y, int64_t rows, int64_t co
         oracle_scan_f32_prod(x + r * cols, y + r * cols, cols, inclusive, 0);
 }
 
+/* ---- segmented scan ---------------------------------------------------------
+ * [Blog2] §7.2 names segmented scans (scans that restart at segment boundaries);
+ * read plainly: the array is cut into consecutive segments, each marked by a head
+ * flag on its first element (element 0 always starts one), and every segment is
+ * scanned on its own with the definitions above, no value crossing a boundary:
+ *   inclusive: y[i] = x[i] if i starts a segment, else y[i-1] (+) x[i]
+ *   exclusive: z[i] = identity if i starts a segment, else z[i-1] (+) x[i-1]
+ * heads[i] != 0 marks a head.  The batched row scan above is the case of a head
+ * every cols elements.  Returns 0, or -1 on an unknown code. */
+int oracle_segmented_u32(const uint32_t *x, uint32_t *y, const uint8_t *heads, int64_t n,
+                         int dtype, int op, int inclusive)
+{
+    if ((dtype != OR_INT32 && dtype != OR_UINT32) || op < OR_SUM || op > OR_AFFINE)
+        return -1;
+    if (op == OR_AFFINE && dtype != OR_UINT32)
+        return -1;
+    uint32_t prev_y = 0, prev_x = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int head = (i == 0) || heads[i] != 0;
+        if (inclusive)
+            y[i] = head ? x[i] : op_u32(dtype, op, prev_y, x[i]);
+        else
+            y[i] = head ? identity_u32(dtype, op) : op_u32(dtype, op, prev_y, prev_x);
+        prev_y = y[i];
+        prev_x = x[i];
+    }
+    return 0;
+}
+
+/* float32 sum: double accumulation; bound[i] = sum of |x[j]| over the segment up
+ * to and including x[i] (the tolerance scale, as for the plain scan). */
+void oracle_segmented_f32_sum(const float *x, double *y, double *bound, const uint8_t *heads,
+                              int64_t n, int inclusive)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)x[i];
+        if (i == 0 || heads[i] != 0) {
+            acc = 0.0;
+            mag = 0.0;
+        }
+        mag += (v < 0.0) ? -v : v;
+        if (inclusive) {
+            acc += v;
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc += v;
+        }
+        if (bound)
+            bound[i] = mag;
+    }
+}
+
+/* float32 max (is_min == 0) or min (is_min != 0), with the tie rule above (the
+ * later element wins) and identity -inf / +inf. */
+void oracle_segmented_f32_minmax(const float *x, float *y, const uint8_t *heads, int64_t n,
+                                 int inclusive, int is_min)
+{
+    uint32_t id_bits = is_min ? 0x7f800000u : 0xff800000u;
+    float id, acc = 0.0f;
+    memcpy(&id, &id_bits, sizeof id);
+    for (int64_t i = 0; i < n; ++i) {
+        if (i == 0 || heads[i] != 0)
+            acc = id;
+        if (inclusive) {
+            acc = is_min ? fmin_right(acc, x[i]) : fmax_right(acc, x[i]);
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc = is_min ? fmin_right(acc, x[i]) : fmax_right(acc, x[i]);
+        }
+    }
+}
+
+/* float32 product in double (relative tolerance, as for the plain product). */
+void oracle_segmented_f32_prod(const float *x, double *y, const uint8_t *heads, int64_t n,
+                               int inclusive)
+{
+    double acc = 1.0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (i == 0 || heads[i] != 0)
+            acc = 1.0;
+        if (inclusive) {
+            acc *= (double)x[i];
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc *= (double)x[i];
+        }
+    }
+}
+
+/* Segments given as offsets (the CSR row-offset array that [Scan3] §一 lists among
+ * scan's uses): segment k covers [offsets[k], offsets[k+1]); offsets[0] = 0,
+ * offsets[nseg] = n, non-decreasing; an empty segment marks nothing.  Writes the
+ * equivalent head flags (heads[] must hold n bytes).  Returns 0, or -1 when the
+ * offsets break those rules. */
+int oracle_heads_from_offsets(const int64_t *offsets, int64_t nseg, uint8_t *heads, int64_t n)
+{
+    if (nseg < 0 || offsets[0] != 0 || offsets[nseg] != n)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        heads[i] = 0;
+    for (int64_t k = 0; k < nseg; ++k) {
+        if (offsets[k + 1] < offsets[k])
+            return -1;
+        if (offsets[k] < n)
+            heads[offsets[k]] = 1;
+    }
+    return 0;
+}
+
 /* ---- radix-sort order and stable sort --------------------------------------
  * The radix sort of the pages ([Scan3] 一: each round places keys by the scan of
  * a digit predicate; [Blog2] 4.2: per-digit histograms, their prefix sums, and a

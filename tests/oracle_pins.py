@@ -342,6 +342,114 @@ def pin_float_product(orc):
     assert orc.scan(xs, "prod", False).y[0] == 1.0
 
 
+# ---------------------------------------------------------------- segmented scan
+
+def _brute_segmented(bits, heads, dtype, op, inclusive):
+    """Each cell recomputed from its own segment: the last head at or before i."""
+    f = brute.op_fn(dtype, op)
+    out = []
+    for i in range(len(bits)):
+        start = max(j for j in range(i + 1) if j == 0 or heads[j])
+        seg = bits[start:i + 1] if inclusive else bits[start:i]
+        acc = brute.identity(dtype, op)
+        for v in seg:
+            acc = f(acc, v)
+        out.append(acc)
+    return out
+
+
+def pin_segmented_special_cases(orc):
+    """Uniform segments are the batched rows; one segment is the plain scan; a head
+    on every element leaves x (inclusive) or the identity (exclusive)."""
+    rng = np.random.default_rng(41)
+    for dtype, op in (("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("uint32", "affine"),
+                      ("int32", "prod"), ("float32", "max"), ("float32", "min")):
+        rows, cols = 7, 13
+        x = wl_case(rng, dtype, op, rows * cols)
+        heads = np.zeros(rows * cols, np.uint8)
+        heads[::cols] = 1
+        for inc in (True, False):
+            seg = orc.segmented(x, op, inc, heads=heads).y
+            bat = orc.batched(x.reshape(rows, cols), op, inc).y.reshape(-1)
+            assert _bits(seg) == _bits(bat)
+            one = orc.segmented(x, op, inc, heads=np.zeros(rows * cols, np.uint8)).y
+            assert _bits(one) == _bits(orc.scan(x, op, inc).y)
+        every = orc.segmented(x, op, True, heads=np.ones(rows * cols, np.uint8)).y
+        assert _bits(every) == _bits(x)
+        ex = orc.segmented(x, op, False, heads=np.full(rows * cols, 7, np.uint8)).y
+        want = _ident(dtype, op) if dtype != "float32" else {"max": 0xFF800000, "min": 0x7F800000}[op]
+        assert all(b == want for b in _bits(ex))
+
+
+def wl_case(rng, dtype, op, n):
+    if dtype == "float32":
+        return rng.integers(-50, 50, n).astype(np.float32)
+    x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    if op == "affine":
+        x |= np.uint32(1 << 16)
+    return x.view(np.int32) if dtype == "int32" else x
+
+
+def pin_segmented_brute_force(orc):
+    rng = np.random.default_rng(43)
+    for dtype in INT_DTYPES:
+        for op in OPS:
+            if not _defined(dtype, op):
+                continue
+            for n in (1, 2, 5, 17, 40):
+                x = wl_case(rng, dtype, op, n)
+                heads = (rng.random(n) < 0.3).astype(np.uint8)
+                for inc in (True, False):
+                    got = _bits(orc.segmented(x, op, inc, heads=heads).y)
+                    assert got == _brute_segmented(_bits(x), heads.tolist(), dtype, op, inc)
+
+
+def pin_segmented_numpy_and_offsets(orc):
+    """int32 sums against numpy (prefix sums minus the sum before each segment), float
+    sums of small integers exactly, and offsets against the equivalent head flags."""
+    rng = np.random.default_rng(47)
+    n = 5000
+    x = rng.integers(-1000, 1000, n).astype(np.int32)
+    starts = np.unique(np.concatenate([[0], rng.integers(0, n, 300)]))
+    heads = np.zeros(n, np.uint8)
+    heads[starts] = 1
+    c = np.cumsum(x.astype(np.int64))
+    seg_of = np.cumsum(heads) - 1                     # segment index of each element
+    before = np.concatenate([[0], c])[starts][seg_of]  # sum of everything before the segment
+    assert np.array_equal(orc.segmented(x, "sum", True, heads=heads).y.astype(np.int64), c - before)
+    assert np.array_equal(orc.segmented(x, "sum", False, heads=heads).y.astype(np.int64),
+                          c - x - before)
+    xf = x.astype(np.float32)
+    r = orc.segmented(xf, "sum", True, heads=heads)
+    assert np.array_equal(r.y, (c - before).astype(np.float64))
+    assert np.all(r.bound >= np.abs(r.y))
+    # offsets, with empty segments (repeated offsets) and a final empty segment
+    offs = np.concatenate([[0], np.sort(rng.integers(0, n, 400)), [n, n]]).astype(np.int64)
+    h2 = np.zeros(n, np.uint8)
+    h2[offs[:-1][offs[:-1] < n]] = 1
+    for op in ("sum", "max", "xor"):
+        for inc in (True, False):
+            a = orc.segmented(x, op, inc, offsets=offs).y
+            b = orc.segmented(x, op, inc, heads=h2).y
+            assert np.array_equal(a, b)
+    # worked example: segments [3 1 4] [1 5] [9 2 6], the last one not empty
+    xe = np.array([3, 1, 4, 1, 5, 9, 2, 6], np.int32)
+    offe = np.array([0, 3, 5, 8], np.int64)
+    assert orc.segmented(xe, "sum", True, offsets=offe).y.tolist() == [3, 4, 8, 1, 6, 9, 11, 17]
+    assert orc.segmented(xe, "sum", False, offsets=offe).y.tolist() == [0, 3, 4, 0, 1, 0, 9, 11]
+    # float max / min ties: the later of equal elements (-0 against +0) is kept
+    z = np.array([0.0, -0.0, 0.0, -0.0, -0.0, 0.0], np.float32)
+    hz = np.array([1, 0, 0, 1, 0, 0], np.uint8)
+    for op in ("max", "min"):
+        assert _bits(orc.segmented(z, op, True, heads=hz).y) == _bits(z)
+    for bad in ([1, n], [0, n - 1], [0, 10, 5, n]):
+        try:
+            orc.segmented(x, "sum", True, offsets=np.array(bad, np.int64))
+        except ValueError:
+            continue
+        raise AssertionError(f"offsets {bad} were accepted")
+
+
 def pin_compaction_brute_and_numpy(orc):
     rng = np.random.default_rng(9)
     cmps = ("lt", "le", "gt", "ge", "eq", "ne")

@@ -23,9 +23,11 @@ MUTANTS = [
     ("uint32_max_signed", "        return (a > b) ? a : b;\n    case OR_MIN:",
      "        return ((int32_t)a > (int32_t)b) ? a : b;\n    case OR_MIN:"),
     ("f32_sum_sign", "acc = (i == 0) ? v : acc + v;", "acc = (i == 0) ? v : acc - v;"),
-    ("f32_exclusive_dropped_term", "            y[i] = acc;\n            acc += v;",
-     "            y[i] = acc;\n            acc = v;"),
-    ("f32_bound_not_abs", "mag += (v < 0.0) ? -v : v;", "mag += v;"),
+    ("f32_exclusive_dropped_term",
+     "acc = (i == 0) ? v : acc + v;\n            y[i] = acc;\n        } else {\n            y[i] = acc;\n            acc += v;",
+     "acc = (i == 0) ? v : acc + v;\n            y[i] = acc;\n        } else {\n            y[i] = acc;\n            acc = v;"),
+    ("f32_bound_not_abs", "        double v = (double)x[i];\n        mag += (v < 0.0) ? -v : v;",
+     "        double v = (double)x[i];\n        mag += v;"),
     ("f32_max_tie_left", "    return (a > b) ? a : b;\n}", "    return (a >= b) ? a : b;\n}"),
     ("f32_max_identity_zero", "uint32_t ninf_bits = 0xff800000u;", "uint32_t ninf_bits = 0u;"),
     ("compact_negated", "        if (pred_holds(dtype, cmp, x[i], thr_bits))\n            out[c++] = x[i];",
@@ -60,6 +62,12 @@ MUTANTS = [
     ("affine_offset_term", "uint32_t b = (a2 * b1 + b2) & 0xffffu;", "uint32_t b = (a1 * b2 + b1) & 0xffffu;"),
     ("f32_min_tie_left", "    return (a < b) ? a : b;\n}\n\nvoid oracle_scan_f32_min",
      "    return (a <= b) ? a : b;\n}\n\nvoid oracle_scan_f32_min"),
+    ("seg_carry_across_head", "        int head = (i == 0) || heads[i] != 0;", "        int head = (i == 0);"),
+    ("seg_exclusive_wrong_operand", "op_u32(dtype, op, prev_y, prev_x);", "op_u32(dtype, op, prev_y, x[i]);"),
+    ("seg_f32_sum_no_restart", "            acc = 0.0;\n            mag = 0.0;", "            mag = 0.0;"),
+    ("seg_minmax_tie_lost", "            acc = is_min ? fmin_right(acc, x[i]) : fmax_right(acc, x[i]);\n            y[i] = acc;",
+     "            acc = is_min ? fmin_right(x[i], acc) : fmax_right(x[i], acc);\n            y[i] = acc;"),
+    ("offsets_drop_last_segment", "    for (int64_t k = 0; k < nseg; ++k) {", "    for (int64_t k = 0; k < nseg - 1; ++k) {"),
     ("f32_prod_exclusive_dropped_term", "            y[i] = acc;\n            acc *= v;",
      "            acc *= v;\n            y[i] = acc;"),
 ]
