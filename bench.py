@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
 ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
-            "blockscans", "sort", "select", "ops")
+            "blockscans", "sort", "select", "ops", "segmented")
 DEFAULT_LEGS = ALL_LEGS
 
 
@@ -237,6 +237,21 @@ def main():
             bw_leg(f"{dt}_{op}_incl_2e26", xs, lambda a, b, op=op: ps.scan_inclusive(a, op, out=b),
                    n, 8 * n)
             del xs
+    if "segmented" in legs:
+        # 2^26 int32 values in segments of random length (mean 1024), inclusive sums
+        n = wl.SIZES["fp32_scan"]
+        g = np.random.default_rng(wl.BASE_SEED + 50)
+        hh = (g.random(n) < 1.0 / 1024).astype(np.uint8)
+        hh[0] = 1
+        offs = np.concatenate([np.flatnonzero(hh), [n]]).astype(np.int64)
+        xs = rotating(lambda i: to_dev(wl.int_uniform(n, 0, 16, seed=700 + i)))
+        hd, od = to_dev(hh), to_dev(offs)
+        bw_leg("segmented_heads_i32_incl_2e26", xs,
+               lambda a, b: ps.segmented_scan(a, "sum", False, heads=hd, out=b), n, 9 * n)
+        bw_leg("segmented_offsets_i32_incl_2e26", xs,
+               lambda a, b: ps.segmented_scan(a, "sum", False, offsets=od, out=b), n,
+               8 * n + 8 * offs.size)
+        del xs, hd, od
     if "rows64" in legs:
         xs = rotating(lambda i: to_dev(wl.rows64()))
         n = xs[0].numel()

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 3
+#define LS_ABI_VERSION 4
 
 typedef enum ls_status {
     LS_OK = 0,
@@ -273,6 +273,42 @@ ls_status ls_radix_sort_workspace_bytes(int64_t n, ls_dtype t, int with_values, 
  * twice and writes them once. */
 ls_status radix_sort(const void *keys_in, void *keys_out, const void *values_in, void *values_out,
                      int64_t n, ls_dtype t, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size for segmented_scan / segmented_scan_offsets.  Errors as for
+ * ls_scan_workspace_bytes. */
+ls_status ls_segmented_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t *bytes);
+
+/* Segmented scan: the array is cut into consecutive segments and each segment is
+ * scanned on its own, no value crossing a boundary ([Blog2] 7.2; the uniform
+ * case is batched_row_scan).
+ *   in, out    n elements; out == in allowed, other overlap is not.
+ *   heads      n bytes; heads[i] != 0 marks the first element of a segment.
+ *              Element 0 always starts one.  Any alignment.
+ *   exclusive  nonzero: out[i] = identity where a segment starts, else the
+ *              operator over the segment's elements before i; zero: inclusive.
+ *   total      NULL or 1 element: the inclusive value of element n-1 (the last
+ *              segment's reduction); the identity for n == 0.
+ *   ws         >= ls_segmented_workspace_bytes(n, t, op) bytes, 16-byte aligned.
+ * Operators, identities and float32 behaviour as for scan_inclusive (float sums
+ * may differ between runs in the last bits).  Errors: LS_ERR_INVALID_ARG for n <
+ * 0, NULL or misaligned buffers with n > 0, overlap (heads or total with out,
+ * ws with anything), unknown enums; LS_ERR_UNSUPPORTED and LS_ERR_WORKSPACE as
+ * for scan_inclusive. */
+ls_status segmented_scan(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                         const uint8_t *heads, void *total, void *ws, size_t ws_bytes, void *stream);
+
+/* Segmented scan with segments given as CSR offsets (the row-offset array of a
+ * sparse matrix, one of scan's uses in [Scan3] 一): segment k is
+ * [offsets[k], offsets[k+1]).
+ *   offsets  nseg + 1 int64 (8-byte aligned), offsets[0] == 0, non-decreasing,
+ *            offsets[nseg] == n; empty segments are allowed.  The kernel reads
+ *            offsets[0 .. nseg-1]; offsets that break these rules give
+ *            unspecified results but no access outside the buffers.
+ *   nseg     >= 1 when n > 0.
+ * Other arguments as for segmented_scan. */
+ls_status segmented_scan_offsets(const void *in, void *out, int64_t n, ls_dtype t, ls_op op,
+                                 int exclusive, const int64_t *offsets, int64_t nseg, void *total,
+                                 void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ __all__ = [
     "compact_if", "batched_row_scan", "workspace_for", "scan_ex", "ls_scan_ex_workspace_bytes",
     "batched_row_scan_ex", "radix_sort", "ls_radix_sort_workspace_bytes", "compact_flags",
     "select_indices_if", "select_indices_flags",
+    "segmented_scan", "ls_segmented_workspace_bytes",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +43,7 @@ if hasattr(torch, "uint32"):
 
 _lock = threading.Lock()
 _lib = None
-ABI_VERSION = 3  # the libscan.h version this binding marshals for
+ABI_VERSION = 4  # the libscan.h version this binding marshals for
 
 
 class LibscanError(RuntimeError):
@@ -87,6 +88,12 @@ def load_library():
         lib.ls_scan_ex_workspace_bytes.argtypes = [I64, I, I, I, ctypes.POINTER(SZ)]
         lib.ls_scan_ex_workspace_bytes.restype = I
         lib.scan_ex.argtypes = [P, P, I64, I, I, I, I, P, P, SZ, P]
+        lib.ls_segmented_workspace_bytes.argtypes = [I64, I, I, ctypes.POINTER(SZ)]
+        lib.ls_segmented_workspace_bytes.restype = I
+        lib.segmented_scan.argtypes = [P, P, I64, I, I, I, P, P, P, SZ, P]
+        lib.segmented_scan.restype = I
+        lib.segmented_scan_offsets.argtypes = [P, P, I64, I, I, I, P, I64, P, P, SZ, P]
+        lib.segmented_scan_offsets.restype = I
         lib.scan_ex.restype = I
         lib.batched_row_scan_ex.argtypes = [P, P, I64, I64, I, I, I, I, P]
         lib.batched_row_scan_ex.restype = I
@@ -202,6 +209,52 @@ def _scan(name: str, x: torch.Tensor, op: str, out, total):
     st = getattr(lib, name)(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], _ptr(total),
                             _ptr(ws), ws.numel(), sh)
     _check(st, name)
+    return out
+
+
+def ls_segmented_workspace_bytes(n: int, dtype: str = "int32", op: str = "sum") -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ls_segmented_workspace_bytes(n, DTYPE_CODES[dtype], OP_CODES[op],
+                                                       ctypes.byref(out)), "ls_segmented_workspace_bytes")
+    return out.value
+
+
+def segmented_scan(x: torch.Tensor, op: str = "sum", exclusive: bool = False,
+                   heads: torch.Tensor | None = None, offsets: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, total: torch.Tensor | None = None) -> torch.Tensor:
+    """Scan each segment of the flattened x on its own.  Segments by `heads` (n bytes,
+    nonzero = first element of a segment; element 0 always starts one) or by
+    `offsets` (int64 CSR offsets, nseg + 1 entries from 0 to n); exactly one of the
+    two.  total (optional, one element): the inclusive value of the last element."""
+    lib = load_library()
+    _require_gpu(x, heads, offsets, out, total)
+    if (heads is None) == (offsets is None):
+        raise ValueError("libscan: give exactly one of heads and offsets")
+    if not x.is_contiguous():
+        raise ValueError("libscan: input must be contiguous")
+    dt = _dtype_of(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != n or not out.is_contiguous():
+        raise ValueError("libscan: out must be a contiguous tensor like the input")
+    if total is not None and (total.dtype != x.dtype or total.numel() < 1):
+        raise ValueError("libscan: total must hold one element of the input dtype")
+    stream, sh = _stream_handle(x.device)
+    ws = workspace_for(x.device, stream, ls_segmented_workspace_bytes(n, dt, op))
+    excl = 1 if exclusive else 0
+    if heads is not None:
+        heads = _flags_tensor(heads, n)
+        st = lib.segmented_scan(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], excl, _ptr(heads),
+                                _ptr(total), _ptr(ws), ws.numel(), sh)
+        _check(st, "segmented_scan")
+    else:
+        if offsets.dtype != torch.int64 or not offsets.is_contiguous() or offsets.numel() < 1:
+            raise ValueError("libscan: offsets must be a contiguous int64 tensor of nseg + 1 entries")
+        st = lib.segmented_scan_offsets(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], excl,
+                                        _ptr(offsets), offsets.numel() - 1, _ptr(total), _ptr(ws),
+                                        ws.numel(), sh)
+        _check(st, "segmented_scan_offsets")
     return out
 
 

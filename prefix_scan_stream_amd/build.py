@@ -29,7 +29,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-paramet
 # Packed fp32 VALU forms are kept out of the generated code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["ls_scan.hip", "ls_compact.hip", "ls_batched.hip", "ls_sort.hip", "ls_api.cpp"]
+SOURCES = ["ls_scan.hip", "ls_compact.hip", "ls_batched.hip", "ls_sort.hip", "ls_segmented.hip",
+           "ls_api.cpp"]
 
 
 def exported_symbols() -> list[str]:

@@ -115,6 +115,57 @@ ls_status compact_common(const void* in, const uint8_t* flags, void* out, int64_
                                                thr, src, pay, ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Shared checks of the segmented scans: head flags (n bytes) when offsets is NULL
+// and by_offsets is false, else CSR offsets (nseg + 1 int64, nseg >= 1 when n > 0).
+ls_status segmented_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                           const uint8_t* heads, const int64_t* offsets, int64_t nseg, bool by_offsets,
+                           void* total, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!size_ok(n) || !valid_dtype(t) || !valid_op(op))
+        return LS_ERR_INVALID_ARG;
+    const size_t bytes = size_t(n) * 4;
+    size_t side_bytes = 0;
+    const void* side = nullptr;
+    if (by_offsets) {
+        if (nseg < 0 || nseg > (INT64_MAX / 8) - 1 || (n > 0 && nseg < 1))
+            return LS_ERR_INVALID_ARG;
+        side = offsets;
+        side_bytes = size_t(nseg + 1) * 8;
+        if (n > 0 && (offsets == nullptr || !aligned(offsets, 8)))
+            return LS_ERR_INVALID_ARG;
+    } else {
+        side = heads;
+        side_bytes = size_t(n);
+        if (n > 0 && heads == nullptr)
+            return LS_ERR_INVALID_ARG;
+    }
+    if (n > 0) {
+        if (in == nullptr || out == nullptr || !aligned(in, 4) || !aligned(out, 4))
+            return LS_ERR_INVALID_ARG;
+        if (in != out && overlaps(in, bytes, out, bytes))
+            return LS_ERR_INVALID_ARG;
+        if (overlaps(side, side_bytes, out, bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (total != nullptr) {
+        if (!aligned(total, 4) || overlaps(total, 4, in, bytes) || overlaps(total, 4, out, bytes) ||
+            overlaps(total, 4, side, side_bytes))
+            return LS_ERR_INVALID_ARG;
+    }
+    if (op_unsupported(t, op))
+        return LS_ERR_UNSUPPORTED;
+    const size_t need = ls::segmented_workspace_bytes(n);
+    ls_status st = check_ws(ws, ws_bytes, need);
+    if (st != LS_OK)
+        return st;
+    if (!aligned(ws, 16) || overlaps(ws, need, in, bytes) || overlaps(ws, need, out, bytes) ||
+        overlaps(ws, need, side, side_bytes) || (total != nullptr && overlaps(ws, need, total, 4)))
+        return LS_ERR_INVALID_ARG;
+    return from_hip(ls::launch_segmented(in, out, n, int(t), int(op), exclusive != 0,
+                                         by_offsets ? nullptr : heads, by_offsets ? offsets : nullptr,
+                                         nseg, total, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +333,31 @@ ls_status radix_sort(const void* keys_in, void* keys_out, const void* values_in,
         return LS_ERR_INVALID_ARG;
     return from_hip(ls::launch_sort(keys_in, keys_out, values_in, values_out, n, int(t), ws,
                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+ls_status ls_segmented_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t* bytes)
+{
+    if (bytes == nullptr || !size_ok(n) || !valid_dtype(t) || !valid_op(op))
+        return LS_ERR_INVALID_ARG;
+    if (op_unsupported(t, op))
+        return LS_ERR_UNSUPPORTED;
+    *bytes = ls::segmented_workspace_bytes(n);
+    return LS_OK;
+}
+
+ls_status segmented_scan(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                         const uint8_t* heads, void* total, void* ws, size_t ws_bytes, void* stream)
+{
+    return segmented_common(in, out, n, t, op, exclusive, heads, nullptr, 0, false, total, ws, ws_bytes,
+                            stream);
+}
+
+ls_status segmented_scan_offsets(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                                 const int64_t* offsets, int64_t nseg, void* total, void* ws,
+                                 size_t ws_bytes, void* stream)
+{
+    return segmented_common(in, out, n, t, op, exclusive, nullptr, offsets, nseg, true, total, ws,
+                            ws_bytes, stream);
 }
 
 }  // extern "C"

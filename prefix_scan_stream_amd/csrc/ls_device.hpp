@@ -501,7 +501,6 @@ constexpr int LB_GROUP = 64;
 template <class Codec>
 __device__ typename Codec::V lookback_grouped(const uint64_t* status, int64_t tile, WsHeader* hdr)
 {
-    using V = typename Codec::V;
     const int lane = lane_id();
     const int64_t g0 = tile - tile % LB_GROUP;  // first tile of this tile's group
     const int before = int(tile - g0);         // tiles of the group before this one

@@ -47,4 +47,11 @@ size_t sort_workspace_bytes(int64_t n, bool with_values);
 hipError_t launch_sort(const void* keys_in, void* keys_out, const void* vals_in, void* vals_out,
                        int64_t n, int dtype, void* ws, hipStream_t stream);
 
+// ---- segmented scan (ls_segmented.hip)
+size_t segmented_workspace_bytes(int64_t n);
+// heads (byte flags) or offsets (nseg + 1 int64, CSR); exactly one is non-null
+hipError_t launch_segmented(const void* in, void* out, int64_t n, int dtype, int op, bool excl,
+                            const uint8_t* heads, const int64_t* offsets, int64_t nseg, void* total,
+                            void* ws, hipStream_t stream);
+
 }  // namespace ls

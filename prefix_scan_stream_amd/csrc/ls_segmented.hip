@@ -1,0 +1,386 @@
+// ls_segmented.hip -- segmented scan in one pass (gfx950).
+//
+// A segmented scan restarts at every segment boundary (lpnh.cn parallel scan
+// overview, section 7.2).  Segments are marked by a head flag on their first
+// element, or given as CSR offsets.  The scan runs the single-pass machinery of
+// the plain scan on (head, value) pairs under the lifted operator
+//     (h1, v1) then (h2, v2)  =  (h1 | h2,  h2 ? v2 : v1 (+) v2),
+// which is associative but not commutative: a head in the later span cuts the
+// earlier value off.  Per tile (16384 elements, 256 threads x 16 runs of 4):
+//   1. take a tile id in start order, load the values (128-bit loads) and the
+//      head bits of every run (flag bytes, or a head bitmap that the tile builds
+//      in LDS from its own range of the offsets);
+//   2. scan each run in registers, restarting at heads; scan the run pairs across
+//      the wave (DPP on the value and the head bit), the (run, wave) pairs in LDS;
+//   3. the first wave publishes the tile's pair and looks back over earlier tiles
+//      for the carry.  A tile that contains a head publishes its full prefix at
+//      once (nothing before the head can reach past it), so segments also cut
+//      the chain of waiting tiles;
+//   4. every element combines the carry into its run with its own in-run value,
+//      unless a head in the run lies at or before it.
+// Elements past n read as 0 and sit after every valid element, as in the plain
+// scan.  HBM traffic: n*4 read + n*4 written, plus n flag bytes or the offsets.
+#include "ls_device.hpp"
+#include "ls_internal.hpp"
+
+namespace ls {
+
+constexpr int SG_BLOCK = 256;
+constexpr int SG_WAVES = SG_BLOCK / 64;
+constexpr int SG_CHUNKS = 16;
+constexpr int SG_TILE = SG_BLOCK * SG_CHUNKS * 4;  // 16384 elements
+
+enum SegSource : int { SEG_FLAGS = 0, SEG_OFFSETS = 1 };
+
+// A (value, head) pair: head != 0 when a segment starts inside the span the
+// value covers (the value then covers only the part from the last head on).
+template <class Op>
+struct SegPair {
+    typename Op::T v;
+    uint32_t h;
+};
+
+template <class Op>
+__device__ __forceinline__ SegPair<Op> seg_identity()
+{
+    return {Op::identity(), 0u};
+}
+
+// earlier then later
+template <class Op>
+__device__ __forceinline__ SegPair<Op> seg_apply(SegPair<Op> a, SegPair<Op> b)
+{
+    return {b.h ? b.v : Op::apply(a.v, b.v), a.h | b.h};
+}
+
+template <int CTRL, int ROW_MASK, class Op>
+__device__ __forceinline__ SegPair<Op> seg_dpp(SegPair<Op> old, SegPair<Op> p)
+{
+    return {dpp_move<CTRL, ROW_MASK>(old.v, p.v), dpp_move<CTRL, ROW_MASK>(old.h, p.h)};
+}
+
+// The wave scan of the plain scan (rows of 16 by row_shr, then the row
+// broadcasts), on pairs.
+template <class Op>
+__device__ __forceinline__ SegPair<Op> seg_wave_inclusive_scan(SegPair<Op> p)
+{
+    const SegPair<Op> id = seg_identity<Op>();
+    p = seg_apply<Op>(seg_dpp<DPP_ROW_SHR1, 0xf>(id, p), p);
+    p = seg_apply<Op>(seg_dpp<DPP_ROW_SHR2, 0xf>(id, p), p);
+    p = seg_apply<Op>(seg_dpp<DPP_ROW_SHR4, 0xf>(id, p), p);
+    p = seg_apply<Op>(seg_dpp<DPP_ROW_SHR8, 0xf>(id, p), p);
+    p = seg_apply<Op>(seg_dpp<DPP_ROW_BCAST15, 0xa>(id, p), p);
+    p = seg_apply<Op>(seg_dpp<DPP_ROW_BCAST31, 0xc>(id, p), p);
+    return p;
+}
+
+template <class Op>
+__device__ __forceinline__ SegPair<Op> seg_wave_shift_up(SegPair<Op> incl)
+{
+    return seg_dpp<DPP_WAVE_SHR1, 0xf>(seg_identity<Op>(), incl);
+}
+
+template <class Op>
+__device__ __forceinline__ SegPair<Op> seg_read_lane(SegPair<Op> p, int lane)
+{
+    return {read_lane(p.v, lane), read_lane(p.h, lane)};
+}
+
+// Status word of a tile: bits 63..62 status flag, bit 32 head, bits 31..0 value.
+template <class Op>
+struct SegCodec {
+    using V = SegPair<Op>;
+    static __device__ __forceinline__ uint32_t flag(uint64_t w) { return uint32_t(w >> 62); }
+    static __device__ __forceinline__ V value(uint64_t w)
+    {
+        return {from_bits<typename Op::T>(uint32_t(w)), uint32_t(w >> 32) & 1u};
+    }
+    static __device__ __forceinline__ uint64_t pack(uint32_t f, V p)
+    {
+        return (uint64_t(f) << 62) | (uint64_t(p.h ? 1u : 0u) << 32) | uint64_t(to_bits(p.v));
+    }
+    static __device__ __forceinline__ V identity() { return seg_identity<Op>(); }
+    static __device__ __forceinline__ V apply(V a, V b) { return seg_apply<Op>(a, b); }
+    static __device__ __forceinline__ V wave_reduce(V part, int /*hi*/)
+    {
+        return seg_read_lane<Op>(seg_wave_inclusive_scan<Op>(part), 63);
+    }
+};
+
+template <class Op, bool INCLUSIVE, bool VEC, int SRC>
+__global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T* __restrict__ in,
+                                                            typename Op::T* __restrict__ out, int64_t n,
+                                                            int64_t num_tiles, const uint8_t* __restrict__ heads,
+                                                            bool heads4, const int64_t* __restrict__ offsets,
+                                                            int64_t nseg, WsHeader* hdr, uint64_t* status,
+                                                            typename Op::T* total)
+{
+    using T = typename Op::T;
+    using P = SegPair<Op>;
+    using Codec = SegCodec<Op>;
+    constexpr int PARTS = SG_CHUNKS * SG_WAVES;
+    constexpr uint32_t RUN_STRIDE = SG_BLOCK * 16u;
+    static_assert(PARTS <= 64, "the (run, wave) pairs are scanned by one wave");
+    __shared__ T s_pv[PARTS];
+    __shared__ uint32_t s_ph[PARTS];
+    __shared__ uint32_t s_tile;
+    __shared__ int64_t s_k0;
+    __shared__ uint32_t s_bits[SRC == SEG_OFFSETS ? SG_TILE / 32 : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const T id = Op::identity();
+
+    if (tid == 0)
+        s_tile = take_tile_id(hdr);
+    __syncthreads();
+    const int64_t tile = s_tile;
+    const int64_t tbase = tile * SG_TILE;
+    const int64_t rem = n - tbase;
+    const uint32_t valid = rem < SG_TILE ? uint32_t(rem) : uint32_t(SG_TILE);
+    const bool full = valid == SG_TILE;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + tbase, valid * 4u);
+    const uint32_t voff = uint32_t(tid) * 16u;
+
+    // 1. values and head bits (bit k of hb[j]: element k of run j starts a segment)
+    Run4<T> r[SG_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < SG_CHUNKS; ++j)
+        r[j] = VEC ? load_run_x4<T>(rin, voff, j * RUN_STRIDE) : load_run_x1<T>(rin, voff, j * RUN_STRIDE);
+    uint32_t hb[SG_CHUNKS];
+    if constexpr (SRC == SEG_OFFSETS) {
+        for (int i = tid; i < SG_TILE / 32; i += SG_BLOCK)
+            s_bits[i] = 0u;
+        if (tid == 0) {
+            // first k in [0, nseg] with offsets[k] >= tbase (offsets non-decreasing)
+            int64_t lo = 0, hi = nseg;
+            while (lo < hi) {
+                const int64_t mid = lo + (hi - lo) / 2;
+                if (offsets[mid] < tbase)
+                    lo = mid + 1;
+                else
+                    hi = mid;
+            }
+            s_k0 = lo;
+        }
+        __syncthreads();
+        for (int64_t k = s_k0 + tid; k < nseg; k += SG_BLOCK) {
+            const int64_t o = offsets[k] - tbase;
+            if (o >= int64_t(valid))
+                break;
+            if (o >= 0)  // malformed (unsorted) offsets may fall before the tile: ignore them
+                atomicOr(&s_bits[o >> 5], 1u << (o & 31));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < SG_CHUNKS; ++j) {
+            const uint32_t e0 = 4u * uint32_t(j * SG_BLOCK + tid);  // 4-aligned: one word
+            hb[j] = (s_bits[e0 >> 5] >> (e0 & 31)) & 0xfu;
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rfl = make_rsrc(heads + tbase, valid);
+#pragma unroll
+        for (int j = 0; j < SG_CHUNKS; ++j) {
+            const uint32_t b0 = 4u * uint32_t(j * SG_BLOCK + tid);
+            uint32_t w;
+            // a dword straddling the end of the range reads as 0 as a whole, so the
+            // run holding a ragged tile's last flags (and unaligned arrays) read bytes
+            if (heads4 && (b0 + 4u <= valid || b0 >= valid)) {
+                w = __builtin_amdgcn_raw_buffer_load_b32(rfl, b0, 0, CACHE_NT);
+            } else {
+                w = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(rfl, b0 + k, 0, CACHE_NT)) << (8 * k);
+            }
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                m |= (((w >> (8 * k)) & 0xffu) != 0u ? 1u : 0u) << k;
+            hb[j] = m;
+        }
+    }
+    if (tile == 0 && tid == 0)
+        hb[0] |= 1u;  // element 0 always starts a segment
+
+    // 2. run scans restarting at heads; wave scan of the run pairs
+    uint32_t wexh = 0;  // bit j: a head in an earlier run of this run's wave row
+    T wexv[SG_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < SG_CHUNKS; ++j) {
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+            r[j].v[k] = ((hb[j] >> k) & 1u) ? r[j].v[k] : Op::apply(r[j].v[k - 1], r[j].v[k]);
+        const P inc = seg_wave_inclusive_scan<Op>(P{r[j].v[3], hb[j] != 0u ? 1u : 0u});
+        const P ex = seg_wave_shift_up<Op>(inc);
+        wexv[j] = ex.v;
+        wexh |= (ex.h ? 1u : 0u) << j;
+        if (lane == 63) {
+            s_pv[j * SG_WAVES + wave] = inc.v;
+            s_ph[j * SG_WAVES + wave] = inc.h;
+        }
+    }
+    __syncthreads();
+
+    // 3. wave 0: scan the (run, wave) pairs, publish, look back for the carry
+    if (wave == 0) {
+        const P part = lane < PARTS ? P{s_pv[lane], s_ph[lane]} : seg_identity<Op>();
+        const P inc = seg_wave_inclusive_scan<Op>(part);
+        const P exc = seg_wave_shift_up<Op>(inc);
+        const P agg = seg_read_lane<Op>(inc, 63);
+        P carry = seg_identity<Op>();
+        if (tile == 0) {
+            if (lane == 0)
+                status_store(status, Codec::pack(ST_PREFIX, agg));
+        } else if (agg.h) {
+            // the tile's inclusive prefix is its own pair: publish it at once
+            if (lane == 0)
+                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, agg));
+            const bool first_is_head = __builtin_amdgcn_readfirstlane(hb[0] & 1u) != 0u;
+            if (!first_is_head)
+                carry = lookback<Codec>(status, tile, hdr);
+        } else {
+            if (lane == 0)
+                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
+            carry = lookback<Codec>(status, tile, hdr);
+            if (lane == 0)
+                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, seg_apply<Op>(carry, agg)));
+        }
+        if (lane < PARTS) {
+            const P c = seg_apply<Op>(carry, exc);
+            s_pv[lane] = c.v;
+            s_ph[lane] = c.h;
+        }
+    }
+    __syncthreads();
+
+    // 4. finish and store; the thread holding element n-1 writes the total (the
+    // inclusive value of element n-1: the last segment's reduction)
+    const int64_t last_local = (tile == num_tiles - 1) ? int64_t(valid) - 1 : -1;
+#pragma unroll
+    for (int j = 0; j < SG_CHUNKS; ++j) {
+        const P sp = {s_pv[j * SG_WAVES + wave], s_ph[j * SG_WAVES + wave]};
+        const T cv = seg_apply<Op>(sp, P{wexv[j], (wexh >> j) & 1u}).v;  // flows into element 0 of the run
+        T incl[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            incl[k] = (hb[j] & ((2u << k) - 1u)) ? r[j].v[k] : Op::apply(cv, r[j].v[k]);
+        Run4<T> o;
+        if constexpr (INCLUSIVE) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o.v[k] = incl[k];
+        } else {
+            o.v[0] = (hb[j] & 1u) ? id : cv;
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+                o.v[k] = ((hb[j] >> k) & 1u) ? id : incl[k - 1];
+        }
+        if (VEC && full)
+            store_run_x4<T>(rout, voff, j * RUN_STRIDE, o);
+        else
+            store_run_x1<T>(rout, voff, j * RUN_STRIDE, o);
+        if (total != nullptr) {
+            const int64_t kk = last_local - 4 * int64_t(j * SG_BLOCK + tid);
+            if (kk >= 0 && kk < 4) {
+                T v = incl[0];  // select, not index: keeps the tile in registers
+#pragma unroll
+                for (int k = 1; k < 4; ++k)
+                    v = (kk == k) ? incl[k] : v;
+                *total = v;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+static int64_t sg_tiles(int64_t n) { return (n + SG_TILE - 1) / SG_TILE; }
+
+size_t segmented_workspace_bytes(int64_t n)
+{
+    const int64_t t = sg_tiles(n);
+    const size_t bytes = sizeof(WsHeader) + size_t(t < 1 ? 1 : t) * STATUS_SLOT_BYTES;
+    return (bytes + 255) & ~size_t(255);
+}
+
+template <class Op>
+__global__ void seg_store_identity_kernel(typename Op::T* total)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0)
+        *total = Op::identity();
+}
+
+template <class Op, int SRC>
+static hipError_t run_segmented(const void* in, void* out, int64_t n, bool excl, const uint8_t* heads,
+                                const int64_t* offsets, int64_t nseg, void* total, void* ws, hipStream_t s)
+{
+    using T = typename Op::T;
+    if (n == 0) {  // no segment: the total is the identity; nothing else to enqueue
+        if (total == nullptr)
+            return hipSuccess;
+        hipLaunchKernelGGL(seg_store_identity_kernel<Op>, dim3(1), dim3(64), 0, s, reinterpret_cast<T*>(total));
+        return hipGetLastError();
+    }
+    const int64_t tiles = sg_tiles(n);
+    hipError_t e = clear_workspace(ws, tiles, s);
+    if (e != hipSuccess)
+        return e;
+    auto* hdr = reinterpret_cast<WsHeader*>(ws);
+    auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
+    const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+    const bool heads4 = (reinterpret_cast<uintptr_t>(heads) & 3) == 0;
+    const T* pin = reinterpret_cast<const T*>(in);
+    T* pout = reinterpret_cast<T*>(out);
+    T* ptot = reinterpret_cast<T*>(total);
+    const dim3 grid(static_cast<uint32_t>(tiles)), block(SG_BLOCK);
+#define LS_SG(INCL, V)                                                                                   \
+    hipLaunchKernelGGL((seg_scan_kernel<Op, INCL, V, SRC>), grid, block, 0, s, pin, pout, n, tiles, heads, \
+                       heads4, offsets, nseg, hdr, status, ptot)
+    if (!excl) {
+        if (vec) LS_SG(true, true); else LS_SG(true, false);
+    } else {
+        if (vec) LS_SG(false, true); else LS_SG(false, false);
+    }
+#undef LS_SG
+    return hipGetLastError();
+}
+
+template <int SRC>
+static hipError_t dispatch_segmented(const void* in, void* out, int64_t n, int dtype, int op, bool excl,
+                                     const uint8_t* heads, const int64_t* offsets, int64_t nseg,
+                                     void* total, void* ws, hipStream_t s)
+{
+#define LS_RUN(OPT) return run_segmented<OPT, SRC>(in, out, n, excl, heads, offsets, nseg, total, ws, s)
+    switch (op) {
+    case OP_SUM: if (dtype == DT_FLOAT32) LS_RUN(SumF32); LS_RUN(SumU32);
+    case OP_XOR: LS_RUN(XorU32);
+    case OP_MAX:
+        if (dtype == DT_INT32) LS_RUN(MaxI32);
+        if (dtype == DT_UINT32) LS_RUN(MaxU32);
+        LS_RUN(MaxF32);
+    case OP_MIN:
+        if (dtype == DT_INT32) LS_RUN(MinI32);
+        if (dtype == DT_UINT32) LS_RUN(MinU32);
+        LS_RUN(MinF32);
+    case OP_AND: LS_RUN(AndU32);
+    case OP_OR: LS_RUN(OrU32);
+    case OP_PROD: if (dtype == DT_FLOAT32) LS_RUN(MulF32); LS_RUN(MulU32);
+    case OP_AFFINE: LS_RUN(AffU32);
+    }
+#undef LS_RUN
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_segmented(const void* in, void* out, int64_t n, int dtype, int op, bool excl,
+                            const uint8_t* heads, const int64_t* offsets, int64_t nseg, void* total,
+                            void* ws, hipStream_t s)
+{
+    if (offsets != nullptr)
+        return dispatch_segmented<SEG_OFFSETS>(in, out, n, dtype, op, excl, nullptr, offsets, nseg, total, ws, s);
+    return dispatch_segmented<SEG_FLAGS>(in, out, n, dtype, op, excl, heads, nullptr, 0, total, ws, s);
+}
+
+}  // namespace ls

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ps.ls_abi_version() == ps.ABI_VERSION == 3
+    assert ps.ls_abi_version() == ps.ABI_VERSION == 4
     for s in range(5):
         assert ps.ls_status_string(s).startswith("LS_")
     assert "unknown" in ps.ls_status_string(99)
@@ -217,6 +217,41 @@ def test_flags_and_indices_validation(lib):
     assert lib.select_indices_flags(None, A_OUT, A_TOT, 10, A_WS, BIG_WS, None) == INV
     assert lib.select_indices_flags(A_F, A_OUT, A_TOT, 1 << 32, A_WS, BIG_WS, None) == INV
     assert lib.select_indices_flags(A_F, A_OUT, A_TOT, 10, None, 0, None) == WS
+
+
+def test_segmented_validation(lib):
+    A_H = 0x7F0070000000
+
+    def sg(inp=A_IN, out=A_OUT, n=10, t=INT32, op=SUM, heads=A_H, total=None, ws=A_WS, wsb=BIG_WS):
+        return lib.segmented_scan(inp, out, n, t, op, 0, heads, total, ws, wsb, None)
+
+    def so(inp=A_IN, out=A_OUT, n=10, t=INT32, op=SUM, offs=A_H, nseg=3, ws=A_WS, wsb=BIG_WS):
+        return lib.segmented_scan_offsets(inp, out, n, t, op, 1, offs, nseg, None, ws, wsb, None)
+
+    assert sg(n=-1) == INV
+    assert sg(heads=None) == INV
+    assert sg(inp=None) == INV
+    assert sg(out=A_IN + 4) == INV                 # partial overlap
+    assert sg(heads=A_OUT + 5) == INV              # heads inside out
+    assert sg(op=8) == INV
+    assert sg(t=F32, op=XOR) == UNS
+    assert sg(t=INT32, op=AFFINE) == UNS
+    assert sg(ws=None) == WS
+    assert sg(heads=A_H + 1, ws=None) == WS        # any heads alignment
+    assert sg(out=A_IN, ws=None) == WS             # in place is allowed
+    assert sg(total=A_OUT + 8) == INV
+    assert so(nseg=0) == INV                        # n > 0 needs a segment
+    assert so(offs=None) == INV
+    assert so(offs=A_H + 4) == INV                  # offsets 8-byte aligned
+    assert so(offs=A_OUT) == INV                    # offsets inside out
+    assert so(ws=None) == WS
+    assert so(n=0, inp=None, out=None, offs=None, nseg=0, ws=None) == WS
+    # empty and no total: valid, and nothing is enqueued
+    assert so(n=0, inp=None, out=None, offs=None, nseg=0) == ps.LS_OK
+    assert sg(n=0, inp=None, out=None, heads=None) == ps.LS_OK
+    sz = ctypes.c_size_t(0)
+    assert lib.ls_segmented_workspace_bytes(1 << 20, INT32, SUM, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert lib.ls_segmented_workspace_bytes(10, F32, AND, ctypes.byref(sz)) == UNS
 
 
 def test_batched_validation(lib):
