@@ -5,29 +5,37 @@
 // scatter (geek-doc.cn parallel prefix scan page, section 一; pgsm.cn SIMT page,
 // section 4.2, which also writes the count on the device).  Here the three steps
 // are fused per tile and the flags and indices never leave the chip:
-//   1. take a tile id in start order, load the tile with 128-bit loads;
-//   2. evaluate the predicate in registers; count kept elements per run of 4,
-//      scan the counts (DPP wave scan + LDS scan of the per-wave totals);
-//   3. stage the kept elements in LDS at their rank inside the tile -- order is
-//      kept, so the result is stable and unique;
-//   4. the first wave looks back over the tile status words for the number of
+//   1. a tile (32768 elements) is loaded with 128-bit loads into registers;
+//   2. the predicate is evaluated in registers; kept elements are counted per run
+//      of 4 and the counts scanned (DPP wave scan, then one wave over the
+//      (run, wave) counts); the tile's total is published at once;
+//   3. the kept elements are staged in LDS at their rank inside the tile -- order
+//      is kept, so the result is stable and unique;
+//   4. a control wave looks back over the tile status words for the number of
 //      elements kept by all earlier tiles (the tile's output offset);
-//   5. copy the staged run from LDS to out[offset ...] with consecutive lanes on
-//      consecutive addresses; the last tile writes the count.
-// No atomics touch the data; the only atomics are the tile-id counter and the
-// status words.  HBM traffic: n*4 bytes read, count*4 bytes written.
+//   5. the staged run is copied from LDS to out[offset ...] with consecutive
+//      lanes on consecutive addresses; the last tile writes the count.
+// Blocks are persistent and pipelined: the next tile's loads and count run while
+// the current tile's look-back does.  No atomics touch the data; the only
+// atomics are the tile-id counter and the status words.  HBM traffic: n*4 bytes
+// read, count*4 bytes written.
 #include "ls_device.hpp"
 #include "ls_internal.hpp"
 
 namespace ls {
 
-constexpr int CP_BLOCK = 256;
-constexpr int CP_WAVES = CP_BLOCK / 64;
+#ifndef LS_CP_BLOCK
+#define LS_CP_BLOCK 512
+#endif
+constexpr int CP_BLOCK = LS_CP_BLOCK;               // data threads per block
+constexpr int CP_WAVES = CP_BLOCK / 64;             // data waves
+constexpr int CP_THREADS = CP_BLOCK + 64;           // data waves + one control wave
 #ifndef LS_CP_CHUNKS
 #define LS_CP_CHUNKS 16
 #endif
-constexpr int CP_CHUNKS = LS_CP_CHUNKS;
-constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;  // 16384 elements (64 KiB staged in LDS) by default
+constexpr int CP_CHUNKS = LS_CP_CHUNKS;             // 16-byte runs per data thread
+constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;   // 32768 elements (128 KiB staged in LDS) by default
+constexpr int CP_LB_WIDE = 16;                      // status words per wide look-back poll
 
 // Predicate through a 4-entry truth table indexed by the comparison outcome:
 // 0 = greater, 1 = less, 2 = equal, 3 = unordered (a NaN is involved).
@@ -36,8 +44,17 @@ __device__ __forceinline__ uint32_t pred_bit(uint32_t v, uint32_t t, uint32_t ta
 {
     int state;
     if constexpr (DT == DT_FLOAT32) {
-        const float a = __builtin_bit_cast(float, v), b = __builtin_bit_cast(float, t);
-        state = (a < b) ? 1 : (a == b) ? 2 : (a > b) ? 0 : 3;
+        // IEEE order through integer keys: -0 is folded into +0, a NaN on either
+        // side is unordered, and the sign-magnitude bits map to an unsigned key
+        // that orders like the values (negative: all bits flipped; otherwise:
+        // the sign bit set).  Same outcomes as float compares, fewer registers.
+        auto key = [](uint32_t u) -> uint32_t {
+            u = (u << 1) == 0u ? 0u : u;
+            return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
+        };
+        const bool nan = (v & 0x7fffffffu) > 0x7f800000u || (t & 0x7fffffffu) > 0x7f800000u;
+        const uint32_t a = key(v), b = key(t);
+        state = nan ? 3 : (a < b) ? 1 : (a == b) ? 2 : 0;
     } else if constexpr (DT == DT_INT32) {
         const int32_t a = int32_t(v), b = int32_t(t);
         state = (a < b) ? 1 : (a == b) ? 2 : 0;
@@ -51,168 +68,279 @@ __device__ __forceinline__ uint32_t pred_bit(uint32_t v, uint32_t t, uint32_t ta
 enum CompactSrc : int { SRC_CMP = 0, SRC_FLAGS = 1 };    // (x CMP thr) / flag byte != 0
 enum CompactPay : int { PAY_VALUE = 0, PAY_INDEX = 1 };  // x itself / its index (uint32)
 
+// The staging buffer is dynamic LDS so that the compiler's occupancy model does
+// not cap the register budget by it (one block per CU either way).
+#ifdef LS_CP_WPE
+#define LS_CP_WAVES_ATTR __attribute__((amdgpu_waves_per_eu(LS_CP_WPE)))
+#else
+#define LS_CP_WAVES_ATTR
+#endif
+
+// Persistent blocks of CP_WAVES data waves and one control wave; a tile is
+// 32768 elements, staged whole in 128 KiB of LDS, one block per CU.  Tiles of a
+// block are numbered k = 0, 1, ... in the order it handles them; at the top of
+// step k, tile k is counted (its tile-local offsets and total are in LDS) and
+// the id of tile k+1 is known.
+//   data waves: stage tile k's kept elements at their ranks, run by run, each
+//     run's registers then taking tile k+1's run, so its loads start with the
+//     staging; count tile k+1 -- the last data wave to finish scans the
+//     (run, wave) counts and publishes the tile's total at once; take the id of
+//     tile k+2 meanwhile (one step ahead, so the counter's latency is hidden).
+//   control wave, meanwhile: tile k's output offset by look-back; publish the
+//     full prefix.
+//   [barrier]  data waves: copy tile k out.  [barrier]
+// The look-back and the copy run while tile k+1 loads.  Tiles of 32768
+// elements halve the tile-id atomics against 16384: one device-scope atomic on
+// one address serializes at about 15 ns, which caps a persistent read of 64 KiB
+// tiles at about 4.3 TB/s on MI355X (6.7 TB/s with the same tiles assigned
+// statically).
 template <int DT, bool VEC, int SRC = SRC_CMP, int PAY = PAY_VALUE, bool FLAG4 = true>
-__global__ __launch_bounds__(CP_BLOCK) void compact_kernel(const uint32_t* __restrict__ in,
-                                                           uint32_t* __restrict__ out, int64_t n,
-                                                           int64_t num_tiles, uint32_t thr,
-                                                           uint32_t table, WsHeader* hdr,
-                                                           uint64_t* status, int64_t* count,
-                                                           const uint8_t* __restrict__ flags)
+LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(const uint32_t* __restrict__ in,
+                                                             uint32_t* __restrict__ out, int64_t n,
+                                                             int64_t num_tiles, uint32_t thr,
+                                                             uint32_t table, WsHeader* hdr,
+                                                             uint64_t* status, int64_t* count,
+                                                             const uint8_t* __restrict__ flags)
 {
-    constexpr int PARTS = CP_CHUNKS * CP_WAVES;  // (run, wave) kept counts per tile
+    constexpr int PARTS = CP_CHUNKS * CP_WAVES;  // (run, wave) kept counts per tile, in element order
+    constexpr int PPL = (PARTS + 63) / 64;       // parts per lane in their scan
     constexpr uint32_t RUN_STRIDE = CP_BLOCK * 16u;
-    static_assert(PARTS <= 64, "the (run, wave) counts are scanned by one wave");
-    __shared__ uint32_t s_items[CP_TILE];
-    __shared__ uint32_t s_part[PARTS];
-    __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_kept;
+    constexpr bool LOAD_VALUES = (SRC == SRC_CMP) || (PAY == PAY_VALUE);
+    static_assert(PARTS % PPL == 0 && PARTS / PPL <= 64, "the (run, wave) counts are scanned by one wave");
+    static_assert((CP_WAVES & (CP_WAVES - 1)) == 0, "arrival counting takes CP_WAVES a power of two");
+    static_assert(CP_CHUNKS <= 16, "keep bits of all runs fit in 64 bits");
+    extern __shared__ uint32_t s_items[];  // CP_TILE words, sized at launch
+    __shared__ uint32_t s_part[2][PARTS];  // tile k's offsets while tile k+1 is counted
+    __shared__ uint32_t s_kept[2];
+    __shared__ uint32_t s_arrive;          // data waves done counting (all tiles so far)
+    __shared__ int64_t s_next[2];          // id of tile k+1, by step parity
     __shared__ int64_t s_base;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-
-    if (tid == 0)
-        s_tile = take_tile_id(hdr);
-    __syncthreads();
-    const int64_t tile = s_tile;
-    const int64_t tbase = tile * CP_TILE;
-    const int64_t rem = n - tbase;
-    const uint32_t valid = rem < CP_TILE ? uint32_t(rem) : uint32_t(CP_TILE);
-    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tbase, valid * 4u);
+    const bool ctrl = wave == CP_WAVES;
     const uint32_t voff = uint32_t(tid) * 16u;
 
-    // 1. load; keep bits in registers (elements past n are never kept)
-    constexpr bool LOAD_VALUES = (SRC == SRC_CMP) || (PAY == PAY_VALUE);
+    auto tile_valid = [&](int64_t t) -> uint32_t {
+        const int64_t rem = n - t * CP_TILE;
+        return rem < CP_TILE ? uint32_t(rem) : uint32_t(CP_TILE);
+    };
+
     Run4<uint32_t> r[CP_CHUNKS];
-    uint32_t keep[CP_CHUNKS];  // bit k: element k of the run is kept
-    if constexpr (LOAD_VALUES) {
-#pragma unroll
-        for (int j = 0; j < CP_CHUNKS; ++j)
+    uint32_t fl[CP_CHUNKS];  // flag bytes of a run (SRC_FLAGS)
+    // packed to spare registers: keep bits 4j..4j+3 = elements of run j kept;
+    // byte j of wex[j / 4] = kept elements of run j in lower lanes of the wave
+    // (at most 63 * 4 = 252)
+    uint64_t keep = 0;
+    uint32_t wex[(CP_CHUNKS + 3) / 4];
+
+    // Loads of run j of tile t (values and / or flag bytes) into r[j] / fl[j].
+    auto load_run = [&](int64_t t, int j) {
+        const int64_t tb = t * CP_TILE;
+        const uint32_t valid = tile_valid(t);
+        if constexpr (LOAD_VALUES) {
+            const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tb, valid * 4u);
             r[j] = VEC ? load_run_x4<uint32_t>(rin, voff, j * RUN_STRIDE)
                        : load_run_x1<uint32_t>(rin, voff, j * RUN_STRIDE);
-    }
-    uint32_t fl[CP_CHUNKS];  // flag bytes of a run (SRC_FLAGS)
-    if constexpr (SRC == SRC_FLAGS) {
-        const __amdgpu_buffer_rsrc_t rfl = make_rsrc(flags + tbase, valid);
-#pragma unroll
-        for (int j = 0; j < CP_CHUNKS; ++j) {
+        }
+        if constexpr (SRC == SRC_FLAGS) {
+            const __amdgpu_buffer_rsrc_t rfl = make_rsrc(flags + tb, valid);
             const uint32_t b0 = 4u * uint32_t(j * CP_BLOCK + tid);
-            // a dword that straddles the end of the range would read as 0 as a whole,
-            // so the one run holding the last flag bytes of a ragged tile loads bytes
+            // a dword that straddles the end of the range would read as 0 as a
+            // whole, so the one run holding the last flag bytes of a ragged tile
+            // loads bytes
             if (FLAG4 && (b0 + 4u <= valid || b0 >= valid)) {
                 fl[j] = __builtin_amdgcn_raw_buffer_load_b32(rfl, b0, 0, CACHE_NT);
             } else {
                 uint32_t w = 0;
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    w |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(rfl, b0 + k, 0, CACHE_NT)) << (8 * k);
+                for (int q = 0; q < 4; ++q)
+                    w |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(rfl, b0 + q, 0, CACHE_NT)) << (8 * q);
                 fl[j] = w;
             }
         }
-    }
-#pragma unroll
-    for (int j = 0; j < CP_CHUNKS; ++j) {
-        const uint32_t e0 = 4u * uint32_t(j * CP_BLOCK + tid);
-        uint32_t m = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t b;
-            if constexpr (SRC == SRC_FLAGS)
-                b = ((fl[j] >> (8 * k)) & 0xffu) != 0u;
-            else
-                b = pred_bit<DT>(r[j].v[k], thr, table);
-            m |= (e0 + k < valid ? b : 0u) << k;
-        }
-        keep[j] = m;
-    }
+    };
 
-    // 2. counts per run, wave scan of the counts, (run, wave) counts to LDS
-    uint32_t wex[CP_CHUNKS];
+    // Keep bits, per-run counts and their wave scans.  The last data wave to arrive turns the (run, wave) counts into
+    // tile-local offsets and publishes the tile's total; no block barrier is
+    // needed, so counting overlaps the control wave's look-back.
+    auto count_tile = [&](int64_t t, int buf) {
+        const uint32_t valid = tile_valid(t);
+        keep = 0;
 #pragma unroll
-    for (int j = 0; j < CP_CHUNKS; ++j) {
-        const uint32_t c = __builtin_popcount(keep[j]);
-        const uint32_t inc = wave_inclusive_scan<SumU32>(c);
-        wex[j] = inc - c;
-        if (lane == 63)
-            s_part[j * CP_WAVES + wave] = inc;
-    }
-    __syncthreads();
-
-    // 3. wave 0: tile-local exclusive offsets of the (run, wave) parts; publish
-    // the tile's count so later tiles can use it before this tile is done
-    if (wave == 0) {
-        const uint32_t v = lane < PARTS ? s_part[lane] : 0u;
-        const uint32_t inc = wave_inclusive_scan<SumU32>(v);
-        const uint32_t kept = read_lane(inc, 63);
-        if (lane < PARTS)
-            s_part[lane] = inc - v;
-        if (lane == 0) {
-            s_kept = kept;
-            status_store(status_word(status, tile), CountCodec::pack(tile == 0 ? ST_PREFIX : ST_AGGREGATE, kept));
-        }
-    }
-    __syncthreads();
-    const uint32_t kept = s_kept;
-
-    // 4. stage kept elements in LDS at their rank inside the tile (input order)
+        for (int j = 0; j < (CP_CHUNKS + 3) / 4; ++j)
+            wex[j] = 0;
+        // elements past n are never kept: only the block's ragged last tile masks,
+        // with one clamp per run (per-element indices would be loop-invariant
+        // registers the compiler keeps live across the whole loop)
+        const bool ragged = valid < uint32_t(CP_TILE);
+        const int32_t lim = int32_t(valid) - 4 * tid;  // run j holds lim - 4 j CP_BLOCK valid elements
 #pragma unroll
-    for (int j = 0; j < CP_CHUNKS; ++j) {
-        uint32_t rank = s_part[j * CP_WAVES + wave] + wex[j];
+        for (int j = 0; j < CP_CHUNKS; ++j) {
+            uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (keep[j] & (1u << k))
-            {
-                if constexpr (PAY == PAY_INDEX)
-                    s_items[rank++] = uint32_t(tbase) + 4u * uint32_t(j * CP_BLOCK + tid) + k;
+            for (int q = 0; q < 4; ++q) {
+                uint32_t b;
+                if constexpr (SRC == SRC_FLAGS)
+                    b = ((fl[j] >> (8 * q)) & 0xffu) != 0u;
                 else
-                    s_items[rank++] = r[j].v[k];
+                    b = pred_bit<DT>(r[j].v[q], thr, table);
+                m |= b << q;
+            }
+            if (ragged) {
+                const int32_t rj = lim - 4 * j * CP_BLOCK;
+                m &= rj >= 4 ? 0xfu : rj <= 0 ? 0u : (1u << rj) - 1u;
+            }
+            keep |= uint64_t(m) << (4 * j);
+        }
+#pragma unroll
+        for (int j = 0; j < CP_CHUNKS; ++j) {
+            const uint32_t c = __builtin_popcount(uint32_t(keep >> (4 * j)) & 0xfu);
+            const uint32_t inc = wave_inclusive_scan<SumU32>(c);
+            wex[j / 4] |= (inc - c) << (8 * (j % 4));
+            if (lane == 63)
+                s_part[buf][j * CP_WAVES + wave] = inc;
+        }
+        uint32_t old = 0;
+        if (lane == 63)  // the lane that wrote this wave's counts releases them
+            old = __hip_atomic_fetch_add(&s_arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        old = __builtin_amdgcn_readlane(old, 63);
+        if ((old & (CP_WAVES - 1)) == CP_WAVES - 1) {
+            uint32_t v[PPL];
+            uint32_t sum = 0;
+#pragma unroll
+            for (int q = 0; q < PPL; ++q) {
+                v[q] = s_part[buf][PPL * lane + q];
+                sum += v[q];
+            }
+            const uint32_t inc = wave_inclusive_scan<SumU32>(sum);
+            const uint32_t kept = read_lane(inc, 63);
+            uint32_t ex = inc - sum;
+#pragma unroll
+            for (int q = 0; q < PPL; ++q) {
+                s_part[buf][PPL * lane + q] = ex;
+                ex += v[q];
+            }
+            if (lane == 0) {
+                s_kept[buf] = kept;
+                status_store(status_word(status, t), CountCodec::pack(t == 0 ? ST_PREFIX : ST_AGGREGATE, kept));
             }
         }
-    }
+    };
 
-    // 5. wave 0: number of elements kept by all earlier tiles (the output offset)
-    if (wave == 0) {
-        int64_t base = 0;
-        if (tile != 0) {
-            base = int64_t(lookback<CountCodec>(status, tile, hdr));
-            if (lane == 0)
-                status_store(status_word(status, tile), CountCodec::pack(ST_PREFIX, uint64_t(base) + kept));
-        }
-        if (lane == 0)
-            s_base = base;
+    // prologue: tile 0 of the block, counted; the id of tile 1
+    if (tid == 0) {
+        s_arrive = 0;
+        s_next[1] = take_tile_id(hdr);
     }
     __syncthreads();
-    const int64_t base = s_base;
-
-    // 6. contiguous copy LDS -> out[base ...]: 32-bit stores up to the first
-    // 16-byte boundary of the output, then 128-bit stores, then a 32-bit tail
-    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + base, kept * 4u);
-    if (VEC) {
-        const uint32_t mis = uint32_t(reinterpret_cast<uintptr_t>(out + base) >> 2) & 3u;
-        uint32_t head = (4u - mis) & 3u;
-        head = head < kept ? head : kept;
-        if (uint32_t(tid) < head)
-            __builtin_amdgcn_raw_buffer_store_b32(s_items[tid], rout, uint32_t(tid) * 4u, 0, STORE_POLICY);
-        const uint32_t groups = (kept - head) >> 2;
-        for (uint32_t g = tid; g < groups; g += CP_BLOCK) {
-            const uint32_t i = head + 4u * g;
-            u32x4 w;
-            w.x = s_items[i];
-            w.y = s_items[i + 1];
-            w.z = s_items[i + 2];
-            w.w = s_items[i + 3];
-            __builtin_amdgcn_raw_buffer_store_b128(w, rout, i * 4u, 0, STORE_POLICY);
-        }
-        const uint32_t i = head + 4u * groups + uint32_t(tid);
-        if (i < kept)
-            __builtin_amdgcn_raw_buffer_store_b32(s_items[i], rout, i * 4u, 0, STORE_POLICY);
-    } else {
-        for (uint32_t i = tid; i < kept; i += CP_BLOCK)
-            __builtin_amdgcn_raw_buffer_store_b32(s_items[i], rout, i * 4u, 0, STORE_POLICY);
+    int64_t cur = s_next[1];
+    if (cur >= num_tiles)
+        return;  // uniform over the block
+    if (!ctrl) {
+        uint32_t g = 0;
+        if (tid == 0)
+            g = take_tile_id(hdr);
+#pragma unroll
+        for (int j = 0; j < CP_CHUNKS; ++j)
+            load_run(cur, j);
+        count_tile(cur, 0);
+        if (tid == 0)
+            s_next[0] = g;
     }
-    if (tile == num_tiles - 1 && tid == 0)
-        *count = base + int64_t(kept);
+    __syncthreads();
+
+    for (uint32_t k = 0;; ++k) {
+        const int buf = int(k & 1);
+        const int64_t tbase = cur * CP_TILE;
+        const int64_t next = s_next[buf];
+        const uint32_t kept = s_kept[buf];
+
+        if (!ctrl) {
+            // stage tile k at its ranks inside the tile (input order); each run's
+            // registers then take tile k+1's run.  The two cases are separate loops
+            // so that the compiler's wait counting sees every load consumed on its
+            // path.
+            auto stage_run = [&](int j) {
+                const uint32_t kj = uint32_t(keep >> (4 * j)) & 0xfu;
+                uint32_t rank = s_part[buf][j * CP_WAVES + wave] + ((wex[j / 4] >> (8 * (j % 4))) & 0xffu);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (kj & (1u << q)) {
+                        if constexpr (PAY == PAY_INDEX)
+                            s_items[rank++] = uint32_t(tbase) + 4u * uint32_t(j * CP_BLOCK + tid) + q;
+                        else
+                            s_items[rank++] = r[j].v[q];
+                    }
+                }
+            };
+            if (next < num_tiles) {
+                uint32_t g = 0;
+                if (tid == 0)
+                    g = take_tile_id(hdr);  // id of tile k+2, used a step from now
+#pragma unroll
+                for (int j = 0; j < CP_CHUNKS; ++j) {
+                    stage_run(j);
+                    load_run(next, j);
+                }
+                count_tile(next, buf ^ 1);
+                if (tid == 0)
+                    s_next[buf ^ 1] = g;
+            } else {
+#pragma unroll
+                for (int j = 0; j < CP_CHUNKS; ++j)
+                    stage_run(j);
+            }
+        } else {
+            int64_t base = 0;
+            if (cur != 0) {
+                base = int64_t(lookback<CountCodec, CP_LB_WIDE>(status, cur, hdr));
+                if (lane == 0)
+                    status_store(status_word(status, cur), CountCodec::pack(ST_PREFIX, uint64_t(base) + kept));
+            }
+            if (lane == 0) {
+                s_base = base;
+                if (cur == num_tiles - 1)
+                    *count = base + int64_t(kept);
+            }
+        }
+        __syncthreads();  // tile k staged, its offset known, tile k+1 counted
+        const int64_t base = s_base;
+
+        if (!ctrl) {
+            // contiguous copy LDS -> out[base ...]: 32-bit stores up to the first
+            // 16-byte boundary of the output, then 128-bit stores, then a 32-bit tail
+            const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + base, kept * 4u);
+            if (VEC) {
+                const uint32_t mis = uint32_t(reinterpret_cast<uintptr_t>(out + base) >> 2) & 3u;
+                uint32_t head = (4u - mis) & 3u;
+                head = head < kept ? head : kept;
+                if (uint32_t(tid) < head)
+                    __builtin_amdgcn_raw_buffer_store_b32(s_items[tid], rout, uint32_t(tid) * 4u, 0, STORE_POLICY);
+                const uint32_t groups = (kept - head) >> 2;
+                for (uint32_t g = tid; g < groups; g += CP_BLOCK) {
+                    const uint32_t i = head + 4u * g;
+                    u32x4 w;
+                    w.x = s_items[i];
+                    w.y = s_items[i + 1];
+                    w.z = s_items[i + 2];
+                    w.w = s_items[i + 3];
+                    __builtin_amdgcn_raw_buffer_store_b128(w, rout, i * 4u, 0, STORE_POLICY);
+                }
+                const uint32_t i = head + 4u * groups + uint32_t(tid);
+                if (i < kept)
+                    __builtin_amdgcn_raw_buffer_store_b32(s_items[i], rout, i * 4u, 0, STORE_POLICY);
+            } else {
+                for (uint32_t i = tid; i < kept; i += CP_BLOCK)
+                    __builtin_amdgcn_raw_buffer_store_b32(s_items[i], rout, i * 4u, 0, STORE_POLICY);
+            }
+        }
+        __syncthreads();  // tile k copied out before tile k+1 is staged over it
+        if (next >= num_tiles)
+            break;
+        cur = next;
+    }
 }
 
 __global__ void store_i64_kernel(int64_t* p, int64_t v)
@@ -250,13 +378,50 @@ static uint32_t truth_table(int cmp)
     return 0u;
 }
 
+// Blocks that fit on the device at once for this kernel (the persistent grid),
+// after allowing the kernel its 128 KiB of dynamic LDS on the current device.
+// Any grid size is correct -- blocks take tiles from the counter until none are
+// left -- so the figure only sets how many tiles are in flight.  Cached per
+// device; 0 on failure (the caller reports it).
+constexpr int CP_MAX_DEVICES = 64;
+
+template <class K>
+static uint32_t resident_blocks(K kernel)
+{
+    static int cached[CP_MAX_DEVICES] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    const bool cacheable = dev >= 0 && dev < CP_MAX_DEVICES;
+    int v = cacheable ? __atomic_load_n(&cached[dev], __ATOMIC_RELAXED) : 0;
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                int(CP_TILE * sizeof(uint32_t))) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, CP_THREADS, CP_TILE * sizeof(uint32_t)) !=
+                hipSuccess)
+            return 0;
+        v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+        if (cacheable)
+            __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+    }
+    return uint32_t(v);
+}
+
 template <int DT, bool VEC, int SRC, int PAY, bool FLAG4>
-static void launch_compact_kernel(dim3 grid, hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n,
+static hipError_t launch_compact_kernel(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n,
                                   int64_t tiles, uint32_t thr, uint32_t table, WsHeader* hdr,
                                   uint64_t* status, int64_t* count, const uint8_t* flags)
 {
-    hipLaunchKernelGGL((compact_kernel<DT, VEC, SRC, PAY, FLAG4>), grid, dim3(CP_BLOCK), 0, s, in, out, n,
-                       tiles, thr, table, hdr, status, count, flags);
+    auto* k = compact_kernel<DT, VEC, SRC, PAY, FLAG4>;
+    const uint32_t cap = resident_blocks(k);
+    if (cap == 0)
+        return hipErrorInvalidConfiguration;
+    const uint32_t grid = tiles < int64_t(cap) ? uint32_t(tiles) : cap;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(CP_THREADS), CP_TILE * sizeof(uint32_t), s, in, out, n, tiles, thr,
+                       table, hdr, status, count, flags);
+    return hipGetLastError();
 }
 
 // src: SRC_CMP / SRC_FLAGS; pay: PAY_VALUE / PAY_INDEX
@@ -279,9 +444,8 @@ hipError_t launch_compact_general(const void* in, const uint8_t* flags, void* ou
     const auto* pin = reinterpret_cast<const uint32_t*>(in);
     auto* pout = reinterpret_cast<uint32_t*>(out);
     const uint32_t table = truth_table(cmp);
-    const dim3 grid(static_cast<uint32_t>(tiles));
 #define LS_CP(DT, V, SRC, PAY, F4) \
-    launch_compact_kernel<DT, V, SRC, PAY, F4>(grid, s, pin, pout, n, tiles, thr, table, hdr, status, count, flags)
+    e = launch_compact_kernel<DT, V, SRC, PAY, F4>(s, pin, pout, n, tiles, thr, table, hdr, status, count, flags)
     if (src == SRC_CMP) {
         if (pay == PAY_VALUE) {
             switch (dtype) {
@@ -306,7 +470,7 @@ hipError_t launch_compact_general(const void* in, const uint8_t* flags, void* ou
         }
     }
 #undef LS_CP
-    return hipGetLastError();
+    return e;
 }
 
 hipError_t launch_compact(const void* in, void* out, int64_t* count, int64_t n, int dtype, int cmp,

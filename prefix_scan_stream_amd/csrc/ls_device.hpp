@@ -431,23 +431,26 @@ struct CountCodec {
 };
 
 // Exclusive prefix of tile `tile` (>= 1), computed by one full wave from the
-// tile status words.  A poll reads a window of 64 tiles, lane l holding tile
-// last - 63 + l.  In the window, the newest tile that has published a full
-// prefix ends the walk: the answer is the operator over it and every newer tile
-// of the window.  Without one, the 64 totals are combined and the window moves
-// 64 tiles back.  An empty word newer than the stopping tile means that tile has
-// not published yet: sleep, then poll again.  The first poll reads only the
-// eight nearest tiles (one 64-byte request per lane group instead of 64 slots),
-// which settles most tiles whose predecessor is already done.  Windows of 128 to
-// 512 words per poll and shorter sleeps were measured slower: the polls
-// themselves load the memory system that the tiles' data also goes through.
+// tile status words.  A poll reads a window of WIDE tiles (at most 64), lane l
+// holding tile last - 63 + l.  In the window, the newest tile that has published
+// a full prefix ends the walk: the answer is the operator over it and every newer
+// tile of the window.  Without one, the window's totals are combined and the
+// window moves WIDE tiles back.  An empty word newer than the stopping tile means
+// that tile has not published yet: sleep, then poll again.  The first poll reads
+// only the eight nearest tiles, which settles tiles whose predecessor is already
+// done.  Every status word sits in its own 256-byte slot, so a poll costs one
+// coherent request per tile read: windows of 128 to 512 words per poll and
+// shorter sleeps were measured slower, because the polls load the memory system
+// that the tiles' data also goes through.  The scan keeps 64; compaction, whose
+// tiles are fewer and larger, polls 16 at a time.
 constexpr int LB_WINDOW = 64;
 constexpr int LB_NEAR = 8;      // tiles read by the first, narrow poll
 constexpr int LB_SLEEP = 32;    // s_sleep units (64 clocks each) between polls
 
-template <class Codec>
+template <class Codec, int WIDE = LB_WINDOW>
 __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHeader* hdr)
 {
+    static_assert(WIDE >= LB_NEAR && WIDE <= LB_WINDOW, "a wide poll reads LB_NEAR to 64 tiles");
     using V = typename Codec::V;
     const int lane = lane_id();
     auto word = [&](int64_t idx) -> uint64_t {
@@ -467,10 +470,12 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
     int64_t last = tile - 1;
     int spins = 0;
     for (;;) {
-        const uint64_t w = word(last - (LB_WINDOW - 1) + lane);
-        const uint64_t has = __ballot(Codec::flag(w) == ST_PREFIX);
+        // lanes 64 - WIDE .. 63 read the WIDE newest tiles not yet combined
+        const bool act = lane >= LB_WINDOW - WIDE;
+        const uint64_t w = act ? word(last - (LB_WINDOW - 1) + lane) : Codec::pack(ST_AGGREGATE, Codec::identity());
+        const uint64_t has = __ballot(act && Codec::flag(w) == ST_PREFIX);
         const int hi = has ? 63 - __builtin_clzll(has) : -1;
-        if (__ballot(lane > hi && Codec::flag(w) == ST_EMPTY)) {
+        if (__ballot(act && lane > hi && Codec::flag(w) == ST_EMPTY)) {
             if (++spins < LOOKBACK_SPIN_LIMIT) {
                 __builtin_amdgcn_s_sleep(LB_SLEEP);
                 continue;
@@ -483,7 +488,7 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
         excl = Codec::apply(Codec::wave_reduce(part, hi), excl);  // older tiles on the left
         if (hi >= 0)
             return excl;
-        last -= LB_WINDOW;
+        last -= WIDE;
     }
 }
 

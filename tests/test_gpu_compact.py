@@ -11,7 +11,7 @@ from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 
 pytestmark = pytest.mark.gpu
 
-TILE = 8192  # the library's tile; sizes below also cover half and quarter tiles
+TILE = 32768  # the library's compaction tile; sizes below also cover half and quarter tiles
 SENTINEL = 0xDEADBEEF
 
 
@@ -33,7 +33,7 @@ def check_compact(x: np.ndarray, cmp: str, thr, *, offset=0):
     assert np.all(bits(got[c:]) == SENTINEL), "wrote beyond the count"
 
 
-@pytest.mark.parametrize("n", [1, 2, 17, 64, 4095, 4096, 4097, TILE - 1, TILE, TILE + 1,
+@pytest.mark.parametrize("n", [1, 2, 17, 64, 4095, 4096, 4097, 8191, 16385, TILE - 1, TILE, TILE + 1,
                                3 * TILE + 5, 70 * TILE + 9, 200_003, 300 * TILE + 11])
 @pytest.mark.parametrize("dtype", ["int32", "uint32", "float32"])
 @pytest.mark.parametrize("cmp", ["lt", "le", "gt", "ge", "eq", "ne"])
