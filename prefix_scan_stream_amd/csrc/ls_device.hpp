@@ -441,8 +441,9 @@ struct CountCodec {
 // done.  Every status word sits in its own 256-byte slot, so a poll costs one
 // coherent request per tile read: windows of 128 to 512 words per poll and
 // shorter sleeps were measured slower, because the polls load the memory system
-// that the tiles' data also goes through.  The scan keeps 64; compaction, whose
-// tiles are fewer and larger, polls 16 at a time.
+// that the tiles' data also goes through.  Narrow windows win on MI355X: the
+// scan polls 8 tiles at a time (347-349 us at 2^28 against 353 for 16 and 367
+// for 64), compaction 16.
 constexpr int LB_WINDOW = 64;
 constexpr int LB_NEAR = 8;      // tiles read by the first, narrow poll
 constexpr int LB_SLEEP = 32;    // s_sleep units (64 clocks each) between polls
@@ -456,9 +457,10 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
     auto word = [&](int64_t idx) -> uint64_t {
         return idx >= 0 ? status_load(status + idx * STATUS_STRIDE) : Codec::pack(ST_PREFIX, Codec::identity());
     };
-    {
+    if constexpr (WIDE > LB_NEAR) {
         // narrow first poll: lanes 56..63 read the eight nearest tiles; the
-        // other lanes stand for tiles that do not take part (identity totals)
+        // other lanes stand for tiles that do not take part (identity totals).
+        // With WIDE == LB_NEAR the loop's first poll reads the same words.
         const bool near = lane >= LB_WINDOW - LB_NEAR;
         const uint64_t w = near ? word(tile - LB_WINDOW + lane) : Codec::pack(ST_AGGREGATE, Codec::identity());
         const uint64_t has = __ballot(near && Codec::flag(w) == ST_PREFIX);

@@ -8,12 +8,13 @@
 // is the design used here, because only it moves the minimum 2*n*4 bytes that
 // bound an HBM-limited scan:
 //   1. a block takes the next tile id (start order, so it only ever waits for
-//      blocks already running) and loads its tile with 128-bit loads;
-//   2. it scans the tile in registers (serial runs of 4, DPP wave scan, LDS scan
-//      of the per-wave totals) and publishes the tile total;
-//   3. its first wave looks back over the preceding tiles, 256 per poll,
-//      combining published totals until it meets a tile that has published its
-//      full prefix, then publishes its own full prefix;
+//      blocks already running) and loads its 32768-element tile with 128-bit
+//      loads;
+//   2. it scans the tile in registers (serial runs of 4, DPP wave scan, one wave
+//      over the (run, wave) totals) and publishes the tile total;
+//   3. its first wave looks back over the preceding tiles, combining published
+//      totals until it meets a tile that has published its full prefix, then
+//      publishes its own full prefix;
 //   4. it writes prefix (+) local scan with 128-bit stores.
 // Each tile status is one 64-bit word (flag + value) so a single atomic access
 // carries both; see ls_device.hpp.
@@ -31,14 +32,28 @@ constexpr int SCAN_WAVES = SCAN_BLOCK / 64;
 #define LS_SCAN_CHUNKS 16
 #endif
 constexpr int SCAN_CHUNKS = LS_SCAN_CHUNKS;           // 128-bit runs per thread
-constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_CHUNKS * 4;  // 16384 elements by default
+constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_CHUNKS * 4;  // 16384 elements (three-phase schemes)
 
 static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanned by one wave");
+
+// The single pass uses 8-wave blocks, 32768-element tiles: each tile takes one
+// device-scope atomic on the tile counter, and those serialize at about 15 ns,
+// which is a large share of a 2^28 scan's time at 16384 tiles.  Halving the tile
+// count: 366 us against 384 us at 2^28, 104 against 114 us at 2^26; 65536-element
+// tiles (16 waves, one block per CU) are slower again (373-381 us).  The
+// registers (about 112 VGPRs) allow two such blocks per CU.
+#ifndef LS_SP_BLOCK
+#define LS_SP_BLOCK 512
+#endif
+constexpr int SP_BLOCK = LS_SP_BLOCK;
+constexpr int SP_WAVES = SP_BLOCK / 64;
+constexpr int SP_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements
+constexpr int SP_LB_WIDE = 8;  // status words per look-back poll
 
 // Tile-local part of the scan, shared by every tile a block processes: serial
 // scan of each run, wave scan of the run totals (exclusive result in wex), and
 // the (run, wave) totals left in LDS by lane 63, in element order.
-template <class Op, int CHUNKS = SCAN_CHUNKS>
+template <class Op, int CHUNKS = SCAN_CHUNKS, int WAVES = SCAN_WAVES>
 __device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[CHUNKS],
                                                 typename Op::T (&wex)[CHUNKS],
                                                 typename Op::T* s_part, int lane, int wave)
@@ -52,7 +67,7 @@ __device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[CHUNKS
         const T inc = wave_inclusive_scan<Op>(r[j].v[3]);
         wex[j] = wave_shift_up<Op>(inc);
         if (lane == 63)
-            s_part[j * SCAN_WAVES + wave] = inc;
+            s_part[j * WAVES + wave] = inc;
     }
 }
 
@@ -64,16 +79,17 @@ __device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[CHUNKS
 // FIXED: the look-back combines a fixed set of words in a fixed order
 // (lookback_grouped), so float results are the same bits on every run.
 template <class Op, bool INCLUSIVE, bool VEC, int CHUNKS, bool FIXED = false>
-__global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
+__global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
     const typename Op::T* in, typename Op::T* out, int64_t n, int64_t num_tiles, WsHeader* hdr,
     uint64_t* status, typename Op::T* total)
 {
     using T = typename Op::T;
     using Codec = ScanCodec<Op>;
-    constexpr int PARTS = CHUNKS * SCAN_WAVES;  // (run, wave) partial totals per tile
-    constexpr int TILE = SCAN_BLOCK * CHUNKS * 4;
-    constexpr uint32_t RUN_STRIDE = SCAN_BLOCK * 16u;
-    static_assert(PARTS <= 64, "the (run, wave) totals are scanned by one wave");
+    constexpr int PARTS = CHUNKS * SP_WAVES;  // (run, wave) partial totals per tile
+    constexpr int PPL = (PARTS + 63) / 64;    // partial totals per lane in their scan
+    constexpr int TILE = SP_BLOCK * CHUNKS * 4;
+    constexpr uint32_t RUN_STRIDE = SP_BLOCK * 16u;
+    static_assert(PARTS % PPL == 0 && PARTS / PPL <= 64, "the (run, wave) totals are scanned by one wave");
     __shared__ T s_part[PARTS + LS_SCAN_LDS_RESERVE];
     __shared__ uint32_t s_tile;
 
@@ -104,13 +120,20 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
 
     // 2. local scan: runs, wave scan of run totals, (run, wave) totals to LDS
     T wex[CHUNKS];
-    scan_tile_local<Op, CHUNKS>(r, wex, s_part, lane, wave);
+    scan_tile_local<Op, CHUNKS, SP_WAVES>(r, wex, s_part, lane, wave);
     __syncthreads();
 
     // 3. wave 0: scan the partial totals (one per lane), publish the tile total,
     // look back for the tile prefix, and leave prefix (+) partial-exclusive in LDS.
     if (wave == 0) {
-        const T v = lane < PARTS ? s_part[lane] : id;
+        // lane l holds partial totals PPL l .. PPL l + PPL - 1, combined in order
+        T pv[PPL];
+        T v = id;
+#pragma unroll
+        for (int q = 0; q < PPL; ++q) {
+            pv[q] = PPL * lane + q < PARTS ? s_part[PPL * lane + q] : id;
+            v = Op::apply(v, pv[q]);
+        }
         const T inc = wave_inclusive_scan<Op>(v);
         const T exc = wave_shift_up<Op>(inc);
         const T agg = read_lane(inc, 63);
@@ -131,12 +154,17 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
         } else {
             if (lane == 0)
                 status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
-            p = lookback<Codec>(status, tile, hdr);
+            p = lookback<Codec, SP_LB_WIDE>(status, tile, hdr);
             if (lane == 0)
                 status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg)));
         }
-        if (lane < PARTS)
-            s_part[lane] = Op::apply(p, exc);
+        T e = Op::apply(p, exc);
+#pragma unroll
+        for (int q = 0; q < PPL; ++q) {
+            if (PPL * lane + q < PARTS)
+                s_part[PPL * lane + q] = e;
+            e = Op::apply(e, pv[q]);
+        }
     }
     __syncthreads();
 
@@ -144,7 +172,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
     const int64_t last_local = (tile == num_tiles - 1) ? int64_t(valid) - 1 : -1;
 #pragma unroll
     for (int j = 0; j < CHUNKS; ++j) {
-        const T cp = Op::apply(s_part[j * SCAN_WAVES + wave], wex[j]);
+        const T cp = Op::apply(s_part[j * SP_WAVES + wave], wex[j]);
         Run4<T> o;
         if constexpr (INCLUSIVE) {
 #pragma unroll
@@ -163,7 +191,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_single_pass_kernel(
         if (total != nullptr) {
             // select, not index: a run-time index into r[] would move the whole
             // tile from registers to per-lane scratch memory
-            const int64_t kk = last_local - 4 * int64_t(j * SCAN_BLOCK + tid);
+            const int64_t kk = last_local - 4 * int64_t(j * SP_BLOCK + tid);
             if (kk >= 0 && kk < 4) {
                 T v = r[j].v[0];
 #pragma unroll
@@ -385,7 +413,7 @@ int64_t scan_tile_elems() { return SCAN_TILE; }
 
 static int64_t num_tiles_for(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
 
-static int64_t single_pass_tiles(int64_t n) { return num_tiles_for(n); }
+static int64_t single_pass_tiles(int64_t n) { return (n + SP_TILE - 1) / SP_TILE; }
 
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -444,7 +472,7 @@ static void launch_single_pass(const void* in, void* out, int64_t n, int64_t til
     const T* pin = reinterpret_cast<const T*>(in);
     T* pout = reinterpret_cast<T*>(out);
     T* ptot = reinterpret_cast<T*>(total);
-    const dim3 grid(static_cast<uint32_t>(tiles)), block(SCAN_BLOCK);
+    const dim3 grid(static_cast<uint32_t>(tiles)), block(SP_BLOCK);
     if (inclusive) {
         if (vec)
             hipLaunchKernelGGL((scan_single_pass_kernel<Op, true, true, CHUNKS, FIXED>), grid, block, 0, s, pin,

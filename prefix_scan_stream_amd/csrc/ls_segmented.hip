@@ -29,6 +29,9 @@ constexpr int SG_BLOCK = 256;
 constexpr int SG_WAVES = SG_BLOCK / 64;
 constexpr int SG_CHUNKS = 16;
 constexpr int SG_TILE = SG_BLOCK * SG_CHUNKS * 4;  // 16384 elements
+constexpr int SG_LB_WIDE = 8;  // status words per look-back poll (8 / 64: 117 / 119 us at 2^26)
+// 8-wave blocks with 32768-element tiles were slower here (131 us): at about 165
+// VGPRs only one such block fits on a CU.
 
 enum SegSource : int { SEG_FLAGS = 0, SEG_OFFSETS = 1 };
 
@@ -240,11 +243,11 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
                 status_store(status_word(status, tile), Codec::pack(ST_PREFIX, agg));
             const bool first_is_head = __builtin_amdgcn_readfirstlane(hb[0] & 1u) != 0u;
             if (!first_is_head)
-                carry = lookback<Codec>(status, tile, hdr);
+                carry = lookback<Codec, SG_LB_WIDE>(status, tile, hdr);
         } else {
             if (lane == 0)
                 status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
-            carry = lookback<Codec>(status, tile, hdr);
+            carry = lookback<Codec, SG_LB_WIDE>(status, tile, hdr);
             if (lane == 0)
                 status_store(status_word(status, tile), Codec::pack(ST_PREFIX, seg_apply<Op>(carry, agg)));
         }

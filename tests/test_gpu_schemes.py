@@ -11,7 +11,8 @@ from gpu_util import DEV, bits, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-TILE = 16384  # the library tile; the sizes span tiles, ragged tails and many tiles
+TILE = 16384  # the three-phase schemes' tile; the sizes span tiles, ragged tails and many tiles
+SP_TILE = 32768  # the single pass's tile
 SCHEMES = ["single_pass", "reduce_then_scan", "scan_then_propagate", "deterministic"]
 COMBOS = [("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("uint32", "max"),
           ("float32", "sum"), ("float32", "max")]
@@ -36,7 +37,7 @@ def check(x, op, inclusive, scheme, *, offset=0, inplace=False):
 
 
 @pytest.mark.parametrize("n", [1, 2, 63, 4097, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, 300_003,
-                               77 * TILE + 13])
+                               SP_TILE - 1, SP_TILE + 1, 77 * TILE + 13])
 @pytest.mark.parametrize("dtype,op", COMBOS)
 @pytest.mark.parametrize("scheme", SCHEMES)
 @pytest.mark.parametrize("inclusive", [True, False], ids=["incl", "excl"])
@@ -66,11 +67,11 @@ def test_scheme_big_scan_workload(scheme):
     check(wl.big_scan(), "sum", False, scheme)
 
 
-GROUP = 64  # tiles per group of the deterministic single pass
+GROUP = 64  # single-pass tiles per group of the deterministic scheme
 
 
 @pytest.mark.parametrize("op", ["sum", "prod"])
-@pytest.mark.parametrize("n", [TILE * GROUP - 1, TILE * GROUP + 1, 3 * TILE * GROUP + 17,
+@pytest.mark.parametrize("n", [SP_TILE * GROUP - 1, SP_TILE * GROUP + 1, 3 * SP_TILE * GROUP + 17,
                                1 << 26])
 def test_deterministic_scheme_is_bitwise_reproducible(op, n):
     """Float sums and products under the fixed-order single pass: within the
@@ -94,8 +95,8 @@ def test_deterministic_scheme_is_bitwise_reproducible(op, n):
             assert np.array_equal(bits(got), bits(first)), "deterministic scan changed between runs"
 
 
-@pytest.mark.parametrize("n", [GROUP * TILE - 1, GROUP * TILE, GROUP * TILE + 1,
-                               2 * GROUP * TILE + TILE + 3, 300 * TILE + 5])
+@pytest.mark.parametrize("n", [GROUP * SP_TILE - 1, GROUP * SP_TILE, GROUP * SP_TILE + 1,
+                               2 * GROUP * SP_TILE + SP_TILE + 3, 300 * TILE + 5])
 def test_deterministic_scheme_keeps_order(n):
     """Affine maps take the fixed-order kernel too: any combine out of order (the
     group prefix on the wrong side, a total of the wrong tile) changes the bits."""
