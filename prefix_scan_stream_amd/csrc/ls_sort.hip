@@ -25,15 +25,24 @@
 
 namespace ls {
 
-constexpr int RS_BLOCK = 256;
+// 8-wave blocks, 8192-key tiles: longer digit runs per tile (32 keys on average)
+// waste fewer partial-line writes in the scatter, and the LDS (43 / 76 KiB for
+// keys / pairs) still allows 3 / 2 blocks per CU.  2^24 keys: 337-344 us against
+// 367 us with 4096-key tiles, pairs 421-426 against 526-530 us; 16384-key tiles
+// (one block per CU) are slower again (383 / 473-478 us).
+#ifndef LS_RS_BLOCK
+#define LS_RS_BLOCK 512
+#endif
+constexpr int RS_BLOCK = LS_RS_BLOCK;
 constexpr int RS_WAVES = RS_BLOCK / 64;
 constexpr int RS_ITEMS = 16;                   // keys per lane
 constexpr int RS_WTILE = 64 * RS_ITEMS;        // 1024 keys per wave
-constexpr int RS_TILE = RS_WAVES * RS_WTILE;   // 4096 keys per block tile
+constexpr int RS_TILE = RS_WAVES * RS_WTILE;   // 8192 keys per block tile
 constexpr int RS_BITS = 8;
 constexpr int RS_DIGITS = 1 << RS_BITS;
 constexpr int RS_PASSES = 32 / RS_BITS;
-static_assert(RS_DIGITS == RS_BLOCK, "one thread per digit in the block-wide steps");
+static_assert(RS_BLOCK >= RS_DIGITS && RS_DIGITS % 64 == 0, "one thread per digit in the block-wide steps");
+constexpr int RS_DWAVES = RS_DIGITS / 64;      // waves whose threads hold one digit each
 
 template <int DT>
 __device__ __forceinline__ uint32_t order_key(uint32_t k)
@@ -65,7 +74,8 @@ __global__ __launch_bounds__(RS_BLOCK) void rs_hist_kernel(const uint32_t* __res
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t tile = blockIdx.x;
-    cnt[tid] = 0;
+    if (tid < RS_DIGITS)
+        cnt[tid] = 0;
     const int64_t base = tile * RS_TILE + int64_t(wave) * RS_WTILE;
     const int64_t rem = n - base;
     const uint32_t valid = rem <= 0 ? 0u : (rem < RS_WTILE ? uint32_t(rem) : uint32_t(RS_WTILE));
@@ -81,7 +91,8 @@ __global__ __launch_bounds__(RS_BLOCK) void rs_hist_kernel(const uint32_t* __res
             atomicAdd(&cnt[digit_of<DT>(k[i], shift)], 1u);
     }
     __syncthreads();
-    hist[int64_t(tid) * tiles + tile] = cnt[tid];
+    if (tid < RS_DIGITS)
+        hist[int64_t(tid) * tiles + tile] = cnt[tid];
 }
 
 // Stable scatter of one block tile:
@@ -111,9 +122,8 @@ __global__ __launch_bounds__(RS_BLOCK) void rs_scatter_kernel(
     const int wave = tid >> 6;
     const int64_t tile = blockIdx.x;
 
-#pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w)
-        wcnt[w][tid] = 0;
+    for (int i = tid; i < RS_WAVES * RS_DIGITS; i += RS_BLOCK)
+        wcnt[i / RS_DIGITS][i % RS_DIGITS] = 0;
     const int64_t tbase = tile * RS_TILE;
     const int64_t trem = n - tbase;
     const uint32_t tvalid = trem < RS_TILE ? uint32_t(trem) : uint32_t(RS_TILE);
@@ -131,8 +141,9 @@ __global__ __launch_bounds__(RS_BLOCK) void rs_scatter_kernel(
         for (int i = 0; i < RS_ITEMS; ++i)
             v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, uint32_t(i * 64 + lane) * 4u, 0, CACHE_NT);
     }
-    const uint32_t d_me = tid;  // the digit this thread handles in the block-wide steps
-    run_dest[d_me] = offs[int64_t(d_me) * tiles + tile];
+    const uint32_t d_me = tid;  // the digit this thread handles in the block-wide steps (tid < RS_DIGITS)
+    if (tid < RS_DIGITS)
+        run_dest[d_me] = offs[int64_t(d_me) * tiles + tile];
     __syncthreads();
 
     // 1. rank inside the wave tile
@@ -157,22 +168,26 @@ __global__ __launch_bounds__(RS_BLOCK) void rs_scatter_kernel(
 
     // 2. per digit: offsets of the waves inside the digit's run, the run's start in
     // the tile (block-wide exclusive scan of the digit totals), its output place
-    uint32_t tot = 0;
+    uint32_t tot = 0, inc = 0;
+    if (wave < RS_DWAVES) {
 #pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w) {
-        const uint32_t c = wcnt[w][d_me];
-        wcnt[w][d_me] = tot;
-        tot += c;
+        for (int w = 0; w < RS_WAVES; ++w) {
+            const uint32_t c = wcnt[w][d_me];
+            wcnt[w][d_me] = tot;
+            tot += c;
+        }
+        inc = wave_inclusive_scan<SumU32>(tot);
+        if (lane == 63)
+            s_wtot[wave] = inc;
     }
-    const uint32_t inc = wave_inclusive_scan<SumU32>(tot);
-    if (lane == 63)
-        s_wtot[wave] = inc;
     __syncthreads();
-    uint32_t wpre = 0;
+    if (wave < RS_DWAVES) {
+        uint32_t wpre = 0;
 #pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w)
-        wpre += (w < wave) ? s_wtot[w] : 0u;
-    run_start[d_me] = wpre + inc - tot;
+        for (int w = 0; w < RS_DWAVES; ++w)
+            wpre += (w < wave) ? s_wtot[w] : 0u;
+        run_start[d_me] = wpre + inc - tot;
+    }
     __syncthreads();
 
     // 3. stage grouped by digit

@@ -11,7 +11,7 @@ from gpu_util import DEV, bits, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-TILE = 1024  # keys per wave tile of the sort
+TILE = 1024  # keys per wave tile of the sort (a block tile is 8 of them)
 
 
 def make_keys(dtype, n, seed, dup):
@@ -49,7 +49,7 @@ def check_sort(keys, with_values=True, inplace=False):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 63, 64, 65, TILE - 1, TILE, TILE + 1, 4 * TILE + 3,
-                               100_003, (1 << 20) + 7])
+                               8 * TILE - 1, 8 * TILE, 8 * TILE + 1, 100_003, (1 << 20) + 7])
 @pytest.mark.parametrize("dtype", ["int32", "uint32", "float32"])
 @pytest.mark.parametrize("dup", [False, True], ids=["spread", "dups"])
 def test_sort_matches_oracle(dtype, dup, n):
