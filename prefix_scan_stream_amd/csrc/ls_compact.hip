@@ -207,11 +207,14 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
             old = __hip_atomic_fetch_add(&s_arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
         old = __builtin_amdgcn_readlane(old, 63);
         if ((old & (CP_WAVES - 1)) == CP_WAVES - 1) {
+            // lane l scans parts PPL l .. PPL l + PPL - 1; lanes past PARTS / PPL
+            // hold none (their indices would run into the LDS words that follow)
             uint32_t v[PPL];
             uint32_t sum = 0;
 #pragma unroll
             for (int q = 0; q < PPL; ++q) {
-                v[q] = s_part[buf][PPL * lane + q];
+                const int i = PPL * lane + q;
+                v[q] = i < PARTS ? s_part[buf][i] : 0u;
                 sum += v[q];
             }
             const uint32_t inc = wave_inclusive_scan<SumU32>(sum);
@@ -219,7 +222,9 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
             uint32_t ex = inc - sum;
 #pragma unroll
             for (int q = 0; q < PPL; ++q) {
-                s_part[buf][PPL * lane + q] = ex;
+                const int i = PPL * lane + q;
+                if (i < PARTS)
+                    s_part[buf][i] = ex;
                 ex += v[q];
             }
             if (lane == 0) {
