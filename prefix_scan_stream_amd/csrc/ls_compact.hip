@@ -35,7 +35,7 @@ constexpr int CP_THREADS = CP_BLOCK + 64;           // data waves + one control 
 #endif
 constexpr int CP_CHUNKS = LS_CP_CHUNKS;             // 16-byte runs per data thread
 constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;   // 32768 elements (128 KiB staged in LDS) by default
-constexpr int CP_LB_WIDE = 16;                      // status words per wide look-back poll
+constexpr int CP_LB_WIDE = 8;                       // status words per look-back poll
 
 // Predicate through a 4-entry truth table indexed by the comparison outcome:
 // 0 = greater, 1 = less, 2 = equal, 3 = unordered (a NaN is involved).

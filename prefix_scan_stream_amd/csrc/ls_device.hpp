@@ -442,8 +442,8 @@ struct CountCodec {
 // coherent request per tile read: windows of 128 to 512 words per poll and
 // shorter sleeps were measured slower, because the polls load the memory system
 // that the tiles' data also goes through.  Narrow windows win on MI355X: the
-// scan polls 8 tiles at a time (347-349 us at 2^28 against 353 for 16 and 367
-// for 64), compaction 16.
+// scan, the segmented scan and compaction poll 8 tiles at a time (scan 2^28:
+// 347-349 us against 353 for 16 and 367 for 64).
 constexpr int LB_WINDOW = 64;
 constexpr int LB_NEAR = 8;      // tiles read by the first, narrow poll
 constexpr int LB_SLEEP = 32;    // s_sleep units (64 clocks each) between polls

@@ -8,8 +8,9 @@
 // them, and a reordering (lpnh.cn parallel scan overview, section 4.2).
 //
 // Here: four passes of 8-bit digits, least significant first.  Each pass is
-//   1. histogram: every block counts the digits of a tile of RS_TILE consecutive
-//      keys in LDS; counts go to hist[digit * tiles + tile] (digit-major);
+//   1. histogram: every block counts the digits of RS_HT tiles of RS_TILE
+//      consecutive keys in LDS; counts go to hist[digit * tiles + tile]
+//      (digit-major);
 //   2. the library's own single-pass exclusive scan over hist -- after it,
 //      hist[d * tiles + t] is where tile t's first key of digit d goes;
 //   3. scatter: each wave walks its quarter of the tile in input order, 64 keys
@@ -64,35 +65,65 @@ __device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift)
 // Block tile t covers keys t*RS_TILE .. +RS_TILE-1; wave w of it the 1024 keys from
 // w*RS_WTILE, key i of lane l at w*RS_WTILE + i*64 + l (a coalesced 256-byte load
 // per group of 64, groups in input order).
+//
+// Histogram: one block counts RS_HT consecutive tiles (the next tile's keys load
+// while the current one is counted) and writes each digit's RS_HT counts as one
+// contiguous run.  One tile per block wrote each 4-byte count to its own line of
+// the digit-major table, which cost 8x the table's bytes in HBM writes.
+constexpr int RS_HT = 4;
+
 template <int DT>
 __global__ __launch_bounds__(RS_BLOCK) void rs_hist_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                            int shift, uint32_t* __restrict__ hist,
                                                            int64_t tiles)
 {
-    __shared__ uint32_t cnt[RS_DIGITS];
+    __shared__ uint32_t cnt[RS_HT][RS_DIGITS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t tile = blockIdx.x;
-    if (tid < RS_DIGITS)
-        cnt[tid] = 0;
-    const int64_t base = tile * RS_TILE + int64_t(wave) * RS_WTILE;
-    const int64_t rem = n - base;
-    const uint32_t valid = rem <= 0 ? 0u : (rem < RS_WTILE ? uint32_t(rem) : uint32_t(RS_WTILE));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(keys + (rem <= 0 ? 0 : base), valid * 4u);
-    uint32_t k[RS_ITEMS];
+    const int64_t t0 = int64_t(blockIdx.x) * RS_HT;
+    for (int i = tid; i < RS_HT * RS_DIGITS; i += RS_BLOCK)
+        cnt[i / RS_DIGITS][i % RS_DIGITS] = 0;
+
+    // keys of the wave's part of tile t (elements past n are not counted)
+    auto load = [&](int64_t t, uint32_t (&k)[RS_ITEMS]) -> uint32_t {
+        const int64_t base = t * RS_TILE + int64_t(wave) * RS_WTILE;
+        const int64_t rem = n - base;
+        const uint32_t valid = rem <= 0 ? 0u : (rem < RS_WTILE ? uint32_t(rem) : uint32_t(RS_WTILE));
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(keys + (rem <= 0 ? 0 : base), valid * 4u);
 #pragma unroll
-    for (int i = 0; i < RS_ITEMS; ++i)
-        k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, uint32_t(i * 64 + lane) * 4u, 0, CACHE_NT);
+        for (int i = 0; i < RS_ITEMS; ++i)
+            k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, uint32_t(i * 64 + lane) * 4u, 0, CACHE_NT);
+        return valid;
+    };
+    uint32_t ka[RS_ITEMS], kb[RS_ITEMS];
+    uint32_t va = load(t0, ka), vb = 0;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < RS_ITEMS; ++i) {
-        if (uint32_t(i * 64 + lane) < valid)
-            atomicAdd(&cnt[digit_of<DT>(k[i], shift)], 1u);
+    for (int lt = 0; lt < RS_HT; ++lt) {
+        uint32_t (&kc)[RS_ITEMS] = (lt & 1) ? kb : ka;
+        uint32_t (&kn)[RS_ITEMS] = (lt & 1) ? ka : kb;
+        const uint32_t vc = (lt & 1) ? vb : va;
+        if (lt + 1 < RS_HT) {
+            const uint32_t v = load(t0 + lt + 1, kn);  // tiles past the end load nothing
+            if (lt & 1)
+                va = v;
+            else
+                vb = v;
+        }
+#pragma unroll
+        for (int i = 0; i < RS_ITEMS; ++i) {
+            if (uint32_t(i * 64 + lane) < vc)
+                atomicAdd(&cnt[lt][digit_of<DT>(kc[i], shift)], 1u);
+        }
     }
     __syncthreads();
-    if (tid < RS_DIGITS)
-        hist[int64_t(tid) * tiles + tile] = cnt[tid];
+    // digit d's counts of tiles t0 .. t0 + RS_HT - 1 are consecutive words
+    for (int i = tid; i < RS_HT * RS_DIGITS; i += RS_BLOCK) {
+        const int d = i / RS_HT, lt = i % RS_HT;
+        if (t0 + lt < tiles)
+            hist[int64_t(d) * tiles + t0 + lt] = cnt[lt][d];
+    }
 }
 
 // Stable scatter of one block tile:
@@ -250,13 +281,14 @@ static hipError_t run_sort(const uint32_t* kin, uint32_t* kout, const uint32_t* 
     p += rs_round(size_t(m) * 4);
     void* scan_ws = p;
     const dim3 grid(static_cast<uint32_t>(tiles)), block(RS_BLOCK);
+    const dim3 hgrid(static_cast<uint32_t>((tiles + RS_HT - 1) / RS_HT));
     const uint32_t* sk = kin;
     const uint32_t* sv = vin;
     for (int pass = 0; pass < RS_PASSES; ++pass) {
         const int shift = pass * RS_BITS;
         uint32_t* dk = (pass % 2 == 0) ? tk : kout;  // the last pass lands in kout
         uint32_t* dv = (pass % 2 == 0) ? tv : vout;
-        hipLaunchKernelGGL((rs_hist_kernel<DT>), grid, block, 0, s, sk, n, shift, hist, tiles);
+        hipLaunchKernelGGL((rs_hist_kernel<DT>), hgrid, block, 0, s, sk, n, shift, hist, tiles);
         hipError_t e = launch_scan(hist, hist, m, DT_UINT32, OP_SUM, false, nullptr, scan_ws,
                                    SCHEME_SINGLE_PASS, s);
         if (e != hipSuccess)

@@ -92,3 +92,32 @@ def test_flags_workload_size():
     out, cnt = ps.compact_flags(to_dev(x), to_dev(f))
     assert int(to_host(cnt)[0]) == wc
     assert np.array_equal(to_host(out)[:wc], want)
+
+
+MANY = 700 * TILE + 13  # more tiles than one wave of resident blocks: blocks loop over tiles
+
+
+@pytest.mark.parametrize("p", [0.02, 0.5, 0.98])
+def test_many_tiles_per_block(p):
+    """Flag compaction and both index selections where every block handles several
+    tiles in turn (its next tile counted while the current one is copied out)."""
+    n = MANY
+    f = flags_for(n, 91, p)
+    x = wl.u32_bits(n, seed=92).view(np.float32)
+    want, wc = oracle.compact_flags(x, f)
+    out = to_dev(np.full(n, SENTINEL, np.uint32).view(np.float32))
+    cnt = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    ps.compact_flags(to_dev(x), to_dev(f), out=out, count=cnt)
+    check_out(out, cnt, want, wc)
+
+    want, wc = oracle.indices(flags=f)
+    out = to_dev(np.full(n, SENTINEL, np.uint32).view(np.int32))
+    ps.select_indices_flags(to_dev(f), out=out, count=cnt)
+    check_out(out, cnt, want.view(np.int32), wc)
+
+    xi = wl.u32_bits(n, seed=93).view(np.int32)
+    thr = int(np.quantile(xi, p))
+    want, wc = oracle.indices(x=xi, cmp="lt", threshold=thr)
+    out = to_dev(np.full(n, SENTINEL, np.uint32).view(np.int32))
+    ps.select_indices_if(to_dev(xi), "lt", thr, out=out, count=cnt)
+    check_out(out, cnt, want.view(np.int32), wc)
