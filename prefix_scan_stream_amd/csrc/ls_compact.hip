@@ -106,7 +106,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
     constexpr int PPL = (PARTS + 63) / 64;       // parts per lane in their scan
     constexpr uint32_t RUN_STRIDE = CP_BLOCK * 16u;
     constexpr bool LOAD_VALUES = (SRC == SRC_CMP) || (PAY == PAY_VALUE);
-    static_assert(PARTS % PPL == 0 && PARTS / PPL <= 64, "the (run, wave) counts are scanned by one wave");
+    static_assert(PARTS <= 64 * PPL, "the (run, wave) counts are scanned by one wave, PPL per lane");
     static_assert((CP_WAVES & (CP_WAVES - 1)) == 0, "arrival counting takes CP_WAVES a power of two");
     static_assert(CP_CHUNKS <= 16, "keep bits of all runs fit in 64 bits");
     extern __shared__ uint32_t s_items[];  // CP_TILE words, sized at launch
