@@ -331,8 +331,8 @@ def main():
         "dtype": "int32",
         "data": "synthetic",
         "config": {"workload": "int32 exclusive sum scan, N=2^28, values U{0..15} (numpy PCG64)",
-                   "n": h["n"], "scheme": "single-pass decoupled look-back",
-                   "tile_elems": 32768},
+                   "n": h["n"], "scheme": "single pass, tile prefixes published by one chasing wave",
+                   "tile_elems": 26624},
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": h["traffic"]},

@@ -96,11 +96,12 @@ typedef enum ls_op {
 typedef enum ls_cmp { LS_LT = 0, LS_LE = 1, LS_GT = 2, LS_GE = 3, LS_EQ = 4, LS_NE = 5 } ls_cmp;
 
 /* Device-wide schemes for scan_ex (the default entry points use the single pass).
- *   LS_SCHEME_SINGLE_PASS          one launch; each tile publishes its total and
- *                                  looks back over earlier tiles' published values
- *                                  (the in-kernel hand-off through flags in global
- *                                  memory that [Scan3] 四 mentions; [SIMT3] 5.1).
- *                                  Moves 2*n*4 bytes.
+ *   LS_SCHEME_SINGLE_PASS          one launch; each tile publishes its total, one
+ *                                  resident wave turns the published totals into
+ *                                  full prefixes in tile order, and each tile reads
+ *                                  its predecessor's (the in-kernel hand-off through
+ *                                  flags in global memory that [Scan3] 四 mentions;
+ *                                  [SIMT3] 5.1).  Moves 2*n*4 bytes.
  *   LS_SCHEME_REDUCE_THEN_SCAN     tile totals, a scan of the totals, a seeded tile
  *                                  scan: three launches, 3*n*4 bytes ([Scan3] 四).
  *   LS_SCHEME_SCAN_THEN_PROPAGATE  tile scans with totals, a scan of the totals, an

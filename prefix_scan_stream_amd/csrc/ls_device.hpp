@@ -399,6 +399,7 @@ struct ScanCodec {
     }
     static __device__ __forceinline__ V identity() { return Op::identity(); }
     static __device__ __forceinline__ V apply(V a, V b) { return Op::apply(a, b); }
+    static __device__ __forceinline__ V wave_scan(V v) { return wave_inclusive_scan<Op>(v); }
     // Combine the lanes' partials in lane order (lanes below `hi` hold identity).
     static __device__ __forceinline__ V wave_reduce(V part, int /*hi*/)
     {
@@ -442,8 +443,10 @@ struct CountCodec {
 // coherent request per tile read: windows of 128 to 512 words per poll and
 // shorter sleeps were measured slower, because the polls load the memory system
 // that the tiles' data also goes through.  Narrow windows win on MI355X: the
-// scan, the segmented scan and compaction poll 8 tiles at a time (scan 2^28:
-// 347-349 us against 353 for 16 and 367 for 64).
+// segmented scan and compaction poll 8 tiles at a time (measured on the plain
+// scan when it still walked back, 2^28: 347-349 us against 353 for 16 and 367
+// for 64, and 355-356 us for windows that double after each window without a
+// full prefix, up to 32 or 64).  The plain scan now uses chased prefixes (below).
 constexpr int LB_WINDOW = 64;
 constexpr int LB_NEAR = 8;      // tiles read by the first, narrow poll
 constexpr int LB_SLEEP = 32;    // s_sleep units (64 clocks each) between polls
@@ -491,6 +494,91 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
         if (hi >= 0)
             return excl;
         last -= WIDE;
+    }
+}
+
+// ---------------------------------------------------------------- chased prefixes
+// The single-pass scan does not let every tile walk back on its own.  One wave
+// (the one that scanned tile 0) stays resident after its tile and moves the
+// "full prefix" frontier forward for everyone: it reads the 64 status words past
+// the frontier in one poll, takes the run of consecutive tiles that have
+// published their totals, scans those totals across the wave, and publishes a
+// full prefix for each of them.  Every other tile publishes its total and then
+// polls one word, its predecessor's, until that word holds a full prefix: its
+// own exclusive prefix.  Only the chasing wave writes full prefixes (besides
+// tile 0), so each tile's prefix is computed once and every tile sees the same
+// value.
+//
+// Why: traced on MI355X (int32 scan of 2^28), walking tiles took 5.7 polls of
+// 8 words each (about 45 status reads) to reach a published prefix, because the
+// prefixes themselves waited on those walks.  Waiting on one word cuts the
+// status reads per tile to a few, and the wait after the last needed load to one
+// chaser cycle plus one poll.  That traffic saving lets smaller tiles pay:
+// 338 us against 348 us for the scan of 2^28 (26624- against 32768-element
+// tiles, each scheme at its best size).  A chaser reading 16 or 32 words per
+// poll cannot keep up with the tiles (458 / 357 us); 128 or 256 words per poll
+// (two or four per lane) are slower as well (358 / 390 us).
+//
+// Progress: the chaser only reads totals, and a tile publishes its total without
+// waiting for anything; a tile with an id is resident, because ids are taken in
+// start order.  So the frontier always reaches every tile, and both loops are
+// bounded like the look-back (the error word reports a cap that is hit).
+constexpr int LB_WAIT_SLEEP = 8;    // s_sleep units between a tile's polls of its predecessor
+constexpr int LB_CHASE_SLEEP = 2;   // between chaser polls that found nothing new
+
+// Exclusive prefix of `tile` (>= 1): the full prefix that the chaser publishes
+// in the status word of tile - 1.  Called by a whole wave; every lane reads the
+// same word.
+template <class Codec>
+__device__ typename Codec::V wait_prefix(const uint64_t* status, int64_t tile, WsHeader* hdr)
+{
+    const uint64_t* p = status + (tile - 1) * STATUS_STRIDE;
+    int spins = 0;
+    for (;;) {
+        const uint64_t w = status_load(p);
+        if (__ballot(Codec::flag(w) == ST_PREFIX))
+            return Codec::value(w);
+        if (++spins >= LOOKBACK_SPIN_LIMIT) {
+            if (lane_id() == 0)
+                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
+            return Codec::identity();  // only reached on a defect; the error word reports it
+        }
+        __builtin_amdgcn_s_sleep(LB_WAIT_SLEEP);
+    }
+}
+
+// Publishes the full prefix of tiles 1 .. num_tiles - 1, in order, given the
+// full prefix of tile 0.  Called by one whole wave, after tile 0 is published.
+template <class Codec>
+__device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V prefix, WsHeader* hdr)
+{
+    using V = typename Codec::V;
+    const int lane = lane_id();
+    int64_t f = 0;  // newest tile with a published full prefix
+    int idle = 0;
+    while (f < num_tiles - 1) {
+        // lane l reads tile f + 1 + l; k = how many of them, from lane 0 on, hold a total
+        const int64_t idx = f + 1 + lane;
+        const bool in = idx < num_tiles;
+        const uint64_t w = in ? status_load(status + idx * STATUS_STRIDE) : 0ull;
+        const uint64_t miss = __ballot(!in || Codec::flag(w) != ST_AGGREGATE);
+        const int k = miss ? __builtin_ctzll(miss) : 64;
+        if (k == 0) {
+            if (++idle >= LOOKBACK_SPIN_LIMIT) {
+                if (lane == 0)
+                    flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
+                return;  // only reached on a defect; the error word reports it
+            }
+            __builtin_amdgcn_s_sleep(LB_CHASE_SLEEP);
+            continue;
+        }
+        idle = 0;
+        // older on the left: prefix (+) totals of tiles f+1 .. f+1+lane
+        const V inc = Codec::apply(prefix, Codec::wave_scan(lane < k ? Codec::value(w) : Codec::identity()));
+        if (lane < k)
+            status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc));
+        prefix = read_lane(inc, k - 1);
+        f += k;
     }
 }
 

@@ -8,13 +8,13 @@
 // is the design used here, because only it moves the minimum 2*n*4 bytes that
 // bound an HBM-limited scan:
 //   1. a block takes the next tile id (start order, so it only ever waits for
-//      blocks already running) and loads its 32768-element tile with 128-bit
+//      blocks already running) and loads its 26624-element tile with 128-bit
 //      loads;
 //   2. it scans the tile in registers (serial runs of 4, DPP wave scan, one wave
 //      over the (run, wave) totals) and publishes the tile total;
-//   3. its first wave looks back over the preceding tiles, combining published
-//      totals until it meets a tile that has published its full prefix, then
-//      publishes its own full prefix;
+//   3. its first wave waits for the full prefix of the previous tile, which one
+//      chasing wave publishes for every tile in order from the published totals
+//      (the wave that scanned tile 0 stays on for this; see ls_device.hpp);
 //   4. it writes prefix (+) local scan with 128-bit stores.
 // Each tile status is one 64-bit word (flag + value) so a single atomic access
 // carries both; see ls_device.hpp.
@@ -36,19 +36,33 @@ constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_CHUNKS * 4;  // 16384 elements (thre
 
 static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanned by one wave");
 
-// The single pass uses 8-wave blocks, 32768-element tiles: each tile takes one
-// device-scope atomic on the tile counter, and those serialize at about 15 ns,
-// which is a large share of a 2^28 scan's time at 16384 tiles.  Halving the tile
-// count: 366 us against 384 us at 2^28, 104 against 114 us at 2^26; 65536-element
-// tiles (16 waves, one block per CU) are slower again (373-381 us).  The
-// registers (about 112 VGPRs) allow two such blocks per CU.
+// The single pass uses 8-wave blocks.  Each tile takes one device-scope atomic on
+// the tile counter (they serialize at about 15 ns), and a tile holds its data in
+// registers until its prefix is known, so the tile size sets both the counter's
+// share of the time and how long the pipeline of resident tiles takes to fill
+// and drain (two blocks per CU: 512 tiles).  With chased prefixes, 13 runs per
+// thread (26624-element tiles) measured best: 2^28 in 338-340 us, against
+// 341-343 for 12 and 14 runs, 345-348 for 16 (32768) and 351 for 8 (16384).  The
+// deterministic scheme keeps 16 runs: its fixed groups of 64 tiles are slower
+// with smaller tiles (float32 2^26: 98 against 100-102 us).  16-wave blocks with
+// 65536-element tiles (one block per CU) were slower (373-381 us).
 #ifndef LS_SP_BLOCK
 #define LS_SP_BLOCK 512
 #endif
 constexpr int SP_BLOCK = LS_SP_BLOCK;
 constexpr int SP_WAVES = SP_BLOCK / 64;
-constexpr int SP_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements
-constexpr int SP_LB_WIDE = 8;  // status words per look-back poll
+constexpr int SP_CHUNKS = 13;
+constexpr int SP_TILE = SP_BLOCK * SP_CHUNKS * 4;          // 26624 elements
+constexpr int SP_FIXED_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements (deterministic)
+
+// How the single pass obtains tile prefixes for Op: chased (ls_device.hpp) or, for
+// the affine maps, by each tile walking back over 8 status words per poll.  The
+// affine maps need about 150 VGPRs, which leaves one block per CU; with 256 tiles
+// in flight they keep the walk and 32768-element tiles.
+template <class Op> constexpr bool sp_chase = true;
+template <> constexpr bool sp_chase<AffU32> = false;
+template <class Op> constexpr int sp_chunks = sp_chase<Op> ? SP_CHUNKS : SCAN_CHUNKS;
+constexpr int SP_LB_WIDE = 8;  // status words per poll of a walking tile
 
 // Tile-local part of the scan, shared by every tile a block processes: serial
 // scan of each run, wave scan of the run totals (exclusive result in wex), and
@@ -124,7 +138,8 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
     __syncthreads();
 
     // 3. wave 0: scan the partial totals (one per lane), publish the tile total,
-    // look back for the tile prefix, and leave prefix (+) partial-exclusive in LDS.
+    // obtain the tile prefix, and leave prefix (+) partial-exclusive in LDS.
+    T agg0 = id;  // tile 0's total: where the chasing wave starts
     if (wave == 0) {
         // lane l holds partial totals PPL l .. PPL l + PPL - 1, combined in order
         T pv[PPL];
@@ -151,12 +166,18 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
         } else if (tile == 0) {
             if (lane == 0)
                 status_store(status, Codec::pack(ST_PREFIX, agg));
+            agg0 = agg;
         } else {
             if (lane == 0)
                 status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
-            p = lookback<Codec, SP_LB_WIDE>(status, tile, hdr);
-            if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg)));
+            if constexpr (sp_chase<Op>) {
+                // the chasing wave turns this total into a full prefix
+                p = wait_prefix<Codec>(status, tile, hdr);
+            } else {
+                p = lookback<Codec, SP_LB_WIDE>(status, tile, hdr);
+                if (lane == 0)
+                    status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg)));
+            }
         }
         T e = Op::apply(p, exc);
 #pragma unroll
@@ -200,6 +221,13 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
                 *total = Op::apply(cp, v);
             }
         }
+    }
+
+    // 5. tile 0's first wave, its own tile written, publishes every later tile's
+    // full prefix (it returns once the last tile's is out)
+    if constexpr (!FIXED && sp_chase<Op>) {
+        if (tile == 0 && wave == 0)
+            chase_prefixes<Codec>(status, num_tiles, agg0, hdr);
     }
 }
 
@@ -413,7 +441,11 @@ int64_t scan_tile_elems() { return SCAN_TILE; }
 
 static int64_t num_tiles_for(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
 
-static int64_t single_pass_tiles(int64_t n) { return (n + SP_TILE - 1) / SP_TILE; }
+static int64_t single_pass_tiles(int64_t n, bool fixed)
+{
+    const int64_t t = fixed ? SP_FIXED_TILE : SP_TILE;  // the smallest tile of each scheme
+    return (n + t - 1) / t;
+}
 
 static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -424,7 +456,7 @@ static size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 size_t scan_workspace_bytes(int64_t n, int scheme)
 {
     if (scheme == SCHEME_SINGLE_PASS || scheme == SCHEME_SINGLE_PASS_FIXED) {
-        const int64_t sp = single_pass_tiles(n);
+        const int64_t sp = single_pass_tiles(n, scheme == SCHEME_SINGLE_PASS_FIXED);
         return round256(sizeof(WsHeader) + size_t(sp < 1 ? 1 : sp) * STATUS_SLOT_BYTES);
     }
     int64_t tiles = num_tiles_for(n);
@@ -500,13 +532,15 @@ static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive,
                                reinterpret_cast<uint32_t*>(total), identity_bits<Op>());
         return hipGetLastError();
     }
-    const int64_t tiles = single_pass_tiles(n);
+    constexpr int CHUNKS = FIXED ? SCAN_CHUNKS : sp_chunks<Op>;
+    constexpr int64_t TILE = int64_t(SP_BLOCK) * CHUNKS * 4;
+    const int64_t tiles = (n + TILE - 1) / TILE;  // never more than the workspace holds
     hipError_t e = clear_workspace(ws, tiles, s);
     if (e != hipSuccess)
         return e;
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
-    launch_single_pass<Op, SCAN_CHUNKS, FIXED>(in, out, n, tiles, inclusive, total, hdr, status, s);
+    launch_single_pass<Op, CHUNKS, FIXED>(in, out, n, tiles, inclusive, total, hdr, status, s);
     return hipGetLastError();
 }
 

@@ -122,7 +122,10 @@ def test_extended_entry_points_validation(lib):
     single = ctypes.c_size_t(0)
     lib.ls_scan_ex_workspace_bytes(1 << 20, F32, SUM, 0, ctypes.byref(single))
     lib.ls_scan_ex_workspace_bytes(1 << 20, F32, SUM, 3, ctypes.byref(sz))
-    assert sz.value == single.value  # the deterministic single pass needs the same workspace
+    # a 256-byte header and one 256-byte status slot per tile: 26624-element tiles for
+    # the single pass, 32768 for the deterministic one
+    assert single.value == 256 + 256 * -(-(1 << 20) // 26624)
+    assert sz.value == 256 + 256 * -(-(1 << 20) // 32768)
     assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, 4, ctypes.byref(sz)) == INV
     assert lib.ls_scan_ex_workspace_bytes(10, F32, XOR, 1, ctypes.byref(sz)) == UNS
     # three-phase workspaces grow with the recursion over the tile totals

@@ -19,9 +19,11 @@ from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 
 pytestmark = pytest.mark.gpu
 
-TILE = 16384  # the three-phase schemes' tile; the single pass's is 2 * TILE
+TILE = 16384     # the three-phase schemes' tile; the deterministic single pass's is 2 * TILE
+SP_TILE = 26624  # the single pass's tile
 SIZES = [1, 2, 3, 63, 64, 65, 1023, 4096, 4097, TILE - 1, TILE, TILE + 1, 2 * TILE - 1, 2 * TILE + 1,
-         3 * TILE + 7, 70 * TILE + 5, 300_003]
+         3 * TILE + 7, 70 * TILE + 5, 300_003, SP_TILE - 1, SP_TILE + 1, 2 * SP_TILE + 1,
+         66 * SP_TILE + 3]
 COMBOS = [("int32", "min"), ("uint32", "min"), ("float32", "min"), ("int32", "and"),
           ("uint32", "and"), ("int32", "or"), ("uint32", "or"), ("int32", "prod"),
           ("uint32", "prod"), ("float32", "prod"), ("uint32", "affine")]

@@ -12,7 +12,7 @@ from gpu_util import DEV, bits, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 TILE = 16384  # the three-phase schemes' tile; the sizes span tiles, ragged tails and many tiles
-SP_TILE = 32768  # the single pass's tile
+SP_TILE = 32768  # the deterministic single pass's tile (groups of 64 such tiles)
 SCHEMES = ["single_pass", "reduce_then_scan", "scan_then_propagate", "deterministic"]
 COMBOS = [("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("uint32", "max"),
           ("float32", "sum"), ("float32", "max")]
