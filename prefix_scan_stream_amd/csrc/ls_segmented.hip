@@ -25,13 +25,23 @@
 
 namespace ls {
 
-constexpr int SG_BLOCK = 256;
+// 8-wave blocks of 8 runs per thread: 16384-element tiles at about 83 VGPRs, two
+// blocks per CU.  A (value, head) pair doubles the scan's registers, so the tile
+// is half the plain scan's.  int32 sums of 2^26 with head flags / CSR offsets:
+// 109-110 / 102 us, against 116-117 / 107 us for 4-wave blocks of 16 runs (the
+// same tile, 160 VGPRs, three blocks per CU), 111-112 / 102-103 us for 10 or 12
+// runs, and 131 us for 16 runs in 8-wave blocks (one block per CU).
+#ifndef LS_SG_BLOCK
+#define LS_SG_BLOCK 512
+#endif
+#ifndef LS_SG_CHUNKS
+#define LS_SG_CHUNKS 8
+#endif
+constexpr int SG_BLOCK = LS_SG_BLOCK;
 constexpr int SG_WAVES = SG_BLOCK / 64;
-constexpr int SG_CHUNKS = 16;
+constexpr int SG_CHUNKS = LS_SG_CHUNKS;
 constexpr int SG_TILE = SG_BLOCK * SG_CHUNKS * 4;  // 16384 elements
 constexpr int SG_LB_WIDE = 8;  // status words per look-back poll (8 / 64: 117 / 119 us at 2^26)
-// 8-wave blocks with 32768-element tiles were slower here (131 us): at about 165
-// VGPRs only one such block fits on a CU.
 
 enum SegSource : int { SEG_FLAGS = 0, SEG_OFFSETS = 1 };
 
@@ -122,8 +132,9 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
     using P = SegPair<Op>;
     using Codec = SegCodec<Op>;
     constexpr int PARTS = SG_CHUNKS * SG_WAVES;
+    constexpr int PPL = (PARTS + 63) / 64;  // (run, wave) pairs per lane in their scan
     constexpr uint32_t RUN_STRIDE = SG_BLOCK * 16u;
-    static_assert(PARTS <= 64, "the (run, wave) pairs are scanned by one wave");
+    static_assert(PARTS % PPL == 0 && PARTS / PPL <= 64, "the (run, wave) pairs are scanned by one wave");
     __shared__ T s_pv[PARTS];
     __shared__ uint32_t s_ph[PARTS];
     __shared__ uint32_t s_tile;
@@ -229,7 +240,15 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
 
     // 3. wave 0: scan the (run, wave) pairs, publish, look back for the carry
     if (wave == 0) {
-        const P part = lane < PARTS ? P{s_pv[lane], s_ph[lane]} : seg_identity<Op>();
+        // lane l holds pairs PPL l .. PPL l + PPL - 1, combined in element order
+        P pv[PPL];
+        P part = seg_identity<Op>();
+#pragma unroll
+        for (int q = 0; q < PPL; ++q) {
+            const int i = PPL * lane + q;
+            pv[q] = i < PARTS ? P{s_pv[i], s_ph[i]} : seg_identity<Op>();
+            part = seg_apply<Op>(part, pv[q]);
+        }
         const P inc = seg_wave_inclusive_scan<Op>(part);
         const P exc = seg_wave_shift_up<Op>(inc);
         const P agg = seg_read_lane<Op>(inc, 63);
@@ -251,10 +270,15 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
             if (lane == 0)
                 status_store(status_word(status, tile), Codec::pack(ST_PREFIX, seg_apply<Op>(carry, agg)));
         }
-        if (lane < PARTS) {
-            const P c = seg_apply<Op>(carry, exc);
-            s_pv[lane] = c.v;
-            s_ph[lane] = c.h;
+        P e = seg_apply<Op>(carry, exc);
+#pragma unroll
+        for (int q = 0; q < PPL; ++q) {
+            const int i = PPL * lane + q;
+            if (i < PARTS) {
+                s_pv[i] = e.v;
+                s_ph[i] = e.h;
+            }
+            e = seg_apply<Op>(e, pv[q]);
         }
     }
     __syncthreads();
