@@ -26,6 +26,11 @@ int64_t scan_tile_elems();
 size_t scan_workspace_bytes(int64_t n, int scheme);
 hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, bool inclusive,
                        void* total, void* ws, int scheme, hipStream_t stream);
+// Single-pass exclusive uint32 sum whose workspace header and first
+// scan_sum_u32_tiles(n) status words the caller has zeroed (n >= 1).
+int64_t scan_sum_u32_tiles(int64_t n);
+hipError_t launch_scan_sum_u32_excl_cleared(const uint32_t* in, uint32_t* out, int64_t n, void* ws,
+                                            hipStream_t stream);
 
 // ---- fused compaction (ls_compact.hip)
 int64_t compact_tile_elems();

@@ -522,6 +522,21 @@ static void launch_single_pass(const void* in, void* out, int64_t n, int64_t til
     }
 }
 
+// Tiles (status slots) of the single-pass uint32 sum over n elements.
+int64_t scan_sum_u32_tiles(int64_t n) { return (n + SP_TILE - 1) / SP_TILE; }
+
+// Exclusive uint32 sum by the single pass, for a caller that has already zeroed the
+// workspace header and the first scan_sum_u32_tiles(n) status words (n >= 1): the
+// radix sort does it inside its histogram kernel and so saves a launch per pass.
+hipError_t launch_scan_sum_u32_excl_cleared(const uint32_t* in, uint32_t* out, int64_t n, void* ws,
+                                            hipStream_t s)
+{
+    auto* hdr = reinterpret_cast<WsHeader*>(ws);
+    auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
+    launch_single_pass<SumU32, SP_CHUNKS, false>(in, out, n, scan_sum_u32_tiles(n), false, nullptr, hdr, status, s);
+    return hipGetLastError();
+}
+
 template <class Op, bool FIXED = false>
 static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive, void* total,
                            void* ws, hipStream_t s)
