@@ -5,6 +5,10 @@
 Objects go to prefix_scan_stream_amd/_build/ (git-ignored); the shared library
 to prefix_scan_stream_amd/libscan.so.  Only the entry points declared in
 include/libscan.h are exported.
+
+build_bounded_wait_test_lib() builds the same sources into libscan_spin1.so with
+every bounded wait (look-back, chased prefixes) giving up after one empty poll.
+Only the test of the workspace error word loads it; the package never does.
 """
 from __future__ import annotations
 
@@ -20,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 HEADER = os.path.join(ROOT, "include", "libscan.h")
 LIB = os.path.join(PKG, "libscan.so")
+SPIN1_LIB = os.path.join(PKG, "libscan_spin1.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -42,34 +47,39 @@ def exported_symbols() -> list[str]:
     return sorted(set(names))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE, "-c", path, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE, *defines, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, f"--offload-arch={ARCH}", "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *defines, f"--offload-arch={ARCH}", "-c", path, "-o", obj]
     subprocess.check_call(cmd)
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, lib: str = LIB, build_dir: str = BUILD, defines: tuple = ()) -> str:
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    vs = os.path.join(BUILD, "exports.map")
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    vs = os.path.join(build_dir, "exports.map")
     with open(vs, "w") as f:
         f.write("{\n  global:\n")
         for name in exported_symbols():
             f.write(f"    {name};\n")
         f.write("  local: *;\n};\n")
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = lib + f".tmp{os.getpid()}"
     subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
                            f"-Wl,--version-script={vs}"])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build_bounded_wait_test_lib(verbose: bool = False) -> str:
+    """libscan_spin1.so: bounded waits give up after one empty poll (test use only)."""
+    return build(verbose, SPIN1_LIB, os.path.join(BUILD, "spin1"), ("-DLS_LOOKBACK_SPIN_LIMIT=1",))
 
 
 if __name__ == "__main__":

@@ -360,7 +360,10 @@ __device__ __forceinline__ uint64_t status_load(const uint64_t* p)
 // Bounded waiting: a look-back gives up after this many empty polls and records
 // the fact in the workspace error word, so a defect can never hang the GPU.  In
 // a correct run the wait is a few microseconds; the cap is far above that.
-constexpr int LOOKBACK_SPIN_LIMIT = 1 << 16;
+#ifndef LS_LOOKBACK_SPIN_LIMIT
+#define LS_LOOKBACK_SPIN_LIMIT (1 << 16)
+#endif
+constexpr int LOOKBACK_SPIN_LIMIT = LS_LOOKBACK_SPIN_LIMIT;  // a test build sets 1 to force the give-up
 constexpr uint32_t WS_ERR_LOOKBACK_TIMEOUT = 1u;
 
 // Workspace header (first 256 bytes of every workspace).
