@@ -49,6 +49,16 @@ def test_library_exports_every_declared_symbol(lib):
     assert exported == set(declared_functions())
 
 
+def test_bounded_wait_test_library_exports_the_same_entry_points():
+    """libscan_spin1.so (the same sources with waits that give up after one poll, for
+    the GPU test of the error word) is built beside libscan.so with the same exports."""
+    if not os.path.exists(psb.SPIN1_LIB):
+        psb.build_bounded_wait_test_lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", psb.SPIN1_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(re.findall(r" T (\w+)$", out, re.M)) == set(declared_functions())
+
+
 def test_version_and_status_strings(lib):
     assert ps.ls_abi_version() == ps.ABI_VERSION == 4
     for s in range(5):
