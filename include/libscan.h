@@ -117,8 +117,9 @@ typedef enum ls_cmp { LS_LT = 0, LS_LE = 1, LS_GT = 2, LS_GE = 3, LS_EQ = 4, LS_
  *                                  a fixed order).  Moves 2*n*4 bytes.
  * The three-phase schemes scan the tile totals recursively when they exceed one
  * tile, as [Scan3] 四 describes for very large arrays.  Their order of combination
- * depends only on n, so they too give the same bits on every run; only
- * LS_SCHEME_SINGLE_PASS combines float values in an order that may vary. */
+ * depends only on n, so they too give the same bits on every run.  So does
+ * LS_SCHEME_SINGLE_PASS: its resident wave combines the tile totals in groups of
+ * 64 tiles aligned to tile 0, in an order fixed by the tile index. */
 typedef enum ls_scheme {
     LS_SCHEME_SINGLE_PASS = 0,
     LS_SCHEME_REDUCE_THEN_SCAN = 1,

@@ -503,10 +503,10 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
 // ---------------------------------------------------------------- chased prefixes
 // The single-pass scan does not let every tile walk back on its own.  One wave
 // (the one that scanned tile 0) stays resident after its tile and moves the
-// "full prefix" frontier forward for everyone: it reads the 64 status words past
-// the frontier in one poll, takes the run of consecutive tiles that have
-// published their totals, scans those totals across the wave, and publishes a
-// full prefix for each of them.  Every other tile publishes its total and then
+// "full prefix" frontier forward for everyone: it polls the status words of the
+// current group of 64 tiles, takes the run of consecutive tiles that have
+// published their totals, scans them across the wave, and publishes a full prefix
+// for each (chase_prefixes below).  Every other tile publishes its total and then
 // polls one word, its predecessor's, until that word holds a full prefix: its
 // own exclusive prefix.  Only the chasing wave writes full prefixes (besides
 // tile 0), so each tile's prefix is computed once and every tile sees the same
@@ -518,9 +518,10 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
 // status reads per tile to a few, and the wait after the last needed load to one
 // chaser cycle plus one poll.  That traffic saving lets smaller tiles pay:
 // 338 us against 348 us for the scan of 2^28 (26624- against 32768-element
-// tiles, each scheme at its best size).  A chaser reading 16 or 32 words per
-// poll cannot keep up with the tiles (458 / 357 us); 128 or 256 words per poll
-// (two or four per lane) are slower as well (358 / 390 us).
+// tiles, each scheme at its best size).  With windows that started at the
+// frontier, a chaser reading 16 or 32 words per poll could not keep up with the
+// tiles (458 / 357 us), and 128 or 256 words per poll (two or four per lane) were
+// slower as well (358 / 390 us).
 //
 // Progress: the chaser only reads totals, and a tile publishes its total without
 // waiting for anything; a tile with an id is resident, because ids are taken in
@@ -552,21 +553,33 @@ __device__ typename Codec::V wait_prefix(const uint64_t* status, int64_t tile, W
 
 // Publishes the full prefix of tiles 1 .. num_tiles - 1, in order, given the
 // full prefix of tile 0.  Called by one whole wave, after tile 0 is published.
+// Tiles form groups of 64 aligned to tile 0, lane l standing for tile 64 G + l.
+// The wave keeps the totals of the group's tiles it has seen in its lanes and
+// polls only the lanes still missing; once lanes 0 .. k-1 hold totals it scans the
+// group across the wave and publishes the new ones on top of the previous group's
+// last full prefix.  Lane j's scan value depends on lanes 0 .. j only, through a
+// tree fixed by j, so every tile's full prefix is a fixed function of the tile
+// totals, whatever a poll happened to find: float results are the same bits on
+// every run (MI355X, float32 sum of 2^26: one distinct result in 10 runs, against
+// 10 in 10 for windows that start at the frontier, at the same speed).
 template <class Codec>
 __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V prefix, WsHeader* hdr)
 {
     using V = typename Codec::V;
     const int lane = lane_id();
-    int64_t f = 0;  // newest tile with a published full prefix
+    int64_t g0 = 0;                                  // first tile of the current group
+    V base = Codec::identity();                      // full prefix of tile g0 - 1
+    V tot = lane == 0 ? prefix : Codec::identity();  // totals of the group's tiles seen so far
+    int have = 1;                                    // lanes 0 .. have-1 hold their totals
     int idle = 0;
-    while (f < num_tiles - 1) {
-        // lane l reads tile f + 1 + l; k = how many of them, from lane 0 on, hold a total
-        const int64_t idx = f + 1 + lane;
-        const bool in = idx < num_tiles;
-        const uint64_t w = in ? status_load(status + idx * STATUS_STRIDE) : 0ull;
-        const uint64_t miss = __ballot(!in || Codec::flag(w) != ST_AGGREGATE);
-        const int k = miss ? __builtin_ctzll(miss) : 64;
-        if (k == 0) {
+    while (g0 + have < num_tiles) {
+        const int64_t idx = g0 + lane;
+        const bool want = lane >= have && idx < num_tiles;
+        const uint64_t w = want ? status_load(status + idx * STATUS_STRIDE) : 0ull;
+        const bool ready = lane < have || (want && Codec::flag(w) == ST_AGGREGATE);
+        const uint64_t miss = __ballot(!ready);
+        const int k = miss ? __builtin_ctzll(miss) : 64;  // lanes 0 .. k-1 now hold totals
+        if (k == have) {
             if (++idle >= LOOKBACK_SPIN_LIMIT) {
                 if (lane == 0)
                     flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
@@ -576,12 +589,19 @@ __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Cod
             continue;
         }
         idle = 0;
-        // older on the left: prefix (+) totals of tiles f+1 .. f+1+lane
-        const V inc = Codec::apply(prefix, Codec::wave_scan(lane < k ? Codec::value(w) : Codec::identity()));
-        if (lane < k)
+        if (lane >= have && lane < k)
+            tot = Codec::value(w);
+        // older on the left: base (+) totals of tiles g0 .. g0 + lane
+        const V inc = Codec::apply(base, Codec::wave_scan(lane < k ? tot : Codec::identity()));
+        if (lane >= have && lane < k)
             status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc));
-        prefix = read_lane(inc, k - 1);
-        f += k;
+        have = k;
+        if (have == 64) {
+            base = read_lane(inc, 63);
+            g0 += 64;
+            have = 0;
+            tot = Codec::identity();
+        }
     }
 }
 

@@ -7,7 +7,7 @@ import torch
 import oracle
 import prefix_scan_stream_amd as ps
 import workloads as wl
-from gpu_util import DEV, bits, to_dev, to_host
+from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +93,36 @@ def test_deterministic_scheme_is_bitwise_reproducible(op, n):
                 assert np.all(np.abs(got - r) <= k * 2.0 ** -23 * np.abs(r) + 1e-30)
         else:
             assert np.array_equal(bits(got), bits(first)), "deterministic scan changed between runs"
+
+
+CHASED_TILE = 26624  # the plain single pass's tile; its prefixes come in groups of 64 tiles
+
+
+@pytest.mark.parametrize("op", ["sum", "prod"])
+@pytest.mark.parametrize("n", [64 * CHASED_TILE - 1, 64 * CHASED_TILE + 1, 3 * 64 * CHASED_TILE + 7,
+                               700 * CHASED_TILE + 5])
+def test_default_single_pass_is_bitwise_reproducible(op, n):
+    """The plain single pass publishes tile prefixes in groups of 64 tiles aligned to
+    tile 0, each prefix a fixed function of the tile totals: float sums and products
+    give the same bits on every run, and stay within the oracle's tolerance."""
+    x = wl.case("float32", op, n, seed=n + 17)
+    xd = to_dev(x)
+    first = None
+    for _ in range(4):
+        got = to_host(ps.scan_inclusive(xd, op))
+        if first is None:
+            first = got.copy()
+            ref = oracle.scan(x, op, True)
+            if op == "sum":
+                ok, worst, k = oracle.fp32_sum_within_tolerance(got, ref)
+                assert ok, f"ratio {worst:.3g} at {k}"
+            else:
+                r = ref.y
+                k = np.arange(1, n + 1, dtype=np.float64)
+                assert np.all(np.abs(got - r) <= k * 2.0 ** -23 * np.abs(r) + 1e-30)
+        else:
+            assert np.array_equal(bits(got), bits(first)), "single-pass scan changed between runs"
+        assert ws_error_word() == 0
 
 
 @pytest.mark.parametrize("n", [GROUP * SP_TILE - 1, GROUP * SP_TILE, GROUP * SP_TILE + 1,
