@@ -383,16 +383,17 @@ static uint32_t truth_table(int cmp)
     return 0u;
 }
 
-// Blocks that fit on the device at once for this kernel (the persistent grid),
-// after allowing the kernel its 128 KiB of dynamic LDS on the current device.
-// Any grid size is correct -- blocks take tiles from the counter until none are
-// left -- so the figure only sets how many tiles are in flight.  Cached per
-// device; 0 on failure (the caller reports it).
+// Blocks of this kernel that fit on the device at once (the persistent grid),
+// after allowing it its 128 KiB of dynamic LDS on the current device.  Any grid
+// size is correct -- blocks take tiles from the counter until none are left -- so
+// the figure only sets how many tiles are in flight.  Cached per device and per
+// kernel (the kernels differ in registers); 0 on failure (the caller reports it).
 constexpr int CP_MAX_DEVICES = 64;
 
-template <class K>
-static uint32_t resident_blocks(K kernel)
+template <int DT, bool VEC, int SRC, int PAY, bool FLAG4>
+static uint32_t resident_blocks()
 {
+    auto* kernel = compact_kernel<DT, VEC, SRC, PAY, FLAG4>;
     static int cached[CP_MAX_DEVICES] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
@@ -420,7 +421,7 @@ static hipError_t launch_compact_kernel(hipStream_t s, const uint32_t* in, uint3
                                   uint64_t* status, int64_t* count, const uint8_t* flags)
 {
     auto* k = compact_kernel<DT, VEC, SRC, PAY, FLAG4>;
-    const uint32_t cap = resident_blocks(k);
+    const uint32_t cap = resident_blocks<DT, VEC, SRC, PAY, FLAG4>();
     if (cap == 0)
         return hipErrorInvalidConfiguration;
     const uint32_t grid = tiles < int64_t(cap) ? uint32_t(tiles) : cap;
