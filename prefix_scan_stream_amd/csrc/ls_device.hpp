@@ -403,6 +403,7 @@ struct ScanCodec {
     static __device__ __forceinline__ V identity() { return Op::identity(); }
     static __device__ __forceinline__ V apply(V a, V b) { return Op::apply(a, b); }
     static __device__ __forceinline__ V wave_scan(V v) { return wave_inclusive_scan<Op>(v); }
+    static __device__ __forceinline__ V lane(V v, int l) { return read_lane(v, l); }
     // Combine the lanes' partials in lane order (lanes below `hi` hold identity).
     static __device__ __forceinline__ V wave_reduce(V part, int /*hi*/)
     {
@@ -561,7 +562,10 @@ __device__ typename Codec::V wait_prefix(const uint64_t* status, int64_t tile, W
 // tree fixed by j, so every tile's full prefix is a fixed function of the tile
 // totals, whatever a poll happened to find: float results are the same bits on
 // every run (MI355X, float32 sum of 2^26: one distinct result in 10 runs, against
-// 10 in 10 for windows that start at the frontier, at the same speed).
+// 10 in 10 for windows that start at the frontier, at the same speed).  A tile
+// whose full prefix does not depend on earlier tiles (a segmented tile containing a
+// head) may publish it itself; the wave takes such a word as that tile's total --
+// its scan gives the same value there -- and does not publish it again.
 template <class Codec>
 __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V prefix, WsHeader* hdr)
 {
@@ -576,7 +580,8 @@ __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Cod
         const int64_t idx = g0 + lane;
         const bool want = lane >= have && idx < num_tiles;
         const uint64_t w = want ? status_load(status + idx * STATUS_STRIDE) : 0ull;
-        const bool ready = lane < have || (want && Codec::flag(w) == ST_AGGREGATE);
+        const bool pub = want && Codec::flag(w) == ST_AGGREGATE;  // still to be published
+        const bool ready = lane < have || pub || (want && Codec::flag(w) == ST_PREFIX);
         const uint64_t miss = __ballot(!ready);
         const int k = miss ? __builtin_ctzll(miss) : 64;  // lanes 0 .. k-1 now hold totals
         if (k == have) {
@@ -593,11 +598,11 @@ __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Cod
             tot = Codec::value(w);
         // older on the left: base (+) totals of tiles g0 .. g0 + lane
         const V inc = Codec::apply(base, Codec::wave_scan(lane < k ? tot : Codec::identity()));
-        if (lane >= have && lane < k)
+        if (lane >= have && lane < k && pub)
             status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc));
         have = k;
         if (have == 64) {
-            base = read_lane(inc, 63);
+            base = Codec::lane(inc, 63);
             g0 += 64;
             have = 0;
             tot = Codec::identity();

@@ -6,16 +6,22 @@
 // the plain scan on (head, value) pairs under the lifted operator
 //     (h1, v1) then (h2, v2)  =  (h1 | h2,  h2 ? v2 : v1 (+) v2),
 // which is associative but not commutative: a head in the later span cuts the
-// earlier value off.  Per tile (16384 elements, 256 threads x 16 runs of 4):
+// earlier value off.  Per tile (16384 elements, 512 threads x 8 runs of 4):
 //   1. take a tile id in start order, load the values (128-bit loads) and the
 //      head bits of every run (flag bytes, or a head bitmap that the tile builds
 //      in LDS from its own range of the offsets);
 //   2. scan each run in registers, restarting at heads; scan the run pairs across
 //      the wave (DPP on the value and the head bit), the (run, wave) pairs in LDS;
-//   3. the first wave publishes the tile's pair and looks back over earlier tiles
-//      for the carry.  A tile that contains a head publishes its full prefix at
-//      once (nothing before the head can reach past it), so segments also cut
-//      the chain of waiting tiles;
+//   3. the first wave publishes the tile's pair and takes its carry from the
+//      chased prefixes (ls_device.hpp): the full prefix of the previous tile.  A
+//      tile that contains a head publishes its full prefix at once (nothing before
+//      the head can reach past it), the others their totals, which the chasing
+//      wave turns into full prefixes in an order fixed by the tile index, so float
+//      sums repeat bit for bit.  A tile whose first element is a head needs no
+//      carry.  Head tiles publishing at once keep most waits short: int32 sums of
+//      2^26 with head flags / CSR offsets 106 / 98 us, against 109-110 / 102-103 us
+//      when every tile walked back (and 113-115 / 109-110 us when head tiles also
+//      waited for the chasing wave);
 //   4. every element combines the carry into its run with its own in-run value,
 //      unless a head in the run lies at or before it.
 // Elements past n read as 0 and sit after every valid element, as in the plain
@@ -41,7 +47,6 @@ constexpr int SG_BLOCK = LS_SG_BLOCK;
 constexpr int SG_WAVES = SG_BLOCK / 64;
 constexpr int SG_CHUNKS = LS_SG_CHUNKS;
 constexpr int SG_TILE = SG_BLOCK * SG_CHUNKS * 4;  // 16384 elements
-constexpr int SG_LB_WIDE = 8;  // status words per look-back poll (8 / 64: 117 / 119 us at 2^26)
 
 enum SegSource : int { SEG_FLAGS = 0, SEG_OFFSETS = 1 };
 
@@ -118,6 +123,8 @@ struct SegCodec {
     {
         return seg_read_lane<Op>(seg_wave_inclusive_scan<Op>(part), 63);
     }
+    static __device__ __forceinline__ V wave_scan(V v) { return seg_wave_inclusive_scan<Op>(v); }
+    static __device__ __forceinline__ V lane(V v, int l) { return seg_read_lane<Op>(v, l); }
 };
 
 template <class Op, bool INCLUSIVE, bool VEC, int SRC>
@@ -238,7 +245,8 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
     }
     __syncthreads();
 
-    // 3. wave 0: scan the (run, wave) pairs, publish, look back for the carry
+    // 3. wave 0: scan the (run, wave) pairs, publish, take the carry
+    P agg0 = seg_identity<Op>();  // tile 0's pair: where the chasing wave starts
     if (wave == 0) {
         // lane l holds pairs PPL l .. PPL l + PPL - 1, combined in element order
         P pv[PPL];
@@ -256,19 +264,13 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
         if (tile == 0) {
             if (lane == 0)
                 status_store(status, Codec::pack(ST_PREFIX, agg));
-        } else if (agg.h) {
-            // the tile's inclusive prefix is its own pair: publish it at once
-            if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, agg));
-            const bool first_is_head = __builtin_amdgcn_readfirstlane(hb[0] & 1u) != 0u;
-            if (!first_is_head)
-                carry = lookback<Codec, SG_LB_WIDE>(status, tile, hdr);
+            agg0 = agg;
         } else {
             if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
-            carry = lookback<Codec, SG_LB_WIDE>(status, tile, hdr);
-            if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, seg_apply<Op>(carry, agg)));
+                status_store(status_word(status, tile), Codec::pack(agg.h ? ST_PREFIX : ST_AGGREGATE, agg));
+            const bool first_is_head = __builtin_amdgcn_readfirstlane(hb[0] & 1u) != 0u;
+            if (!first_is_head)
+                carry = wait_prefix<Codec>(status, tile, hdr);
         }
         P e = seg_apply<Op>(carry, exc);
 #pragma unroll
@@ -320,6 +322,10 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
             }
         }
     }
+    // 5. tile 0's first wave, its own tile written, publishes the later tiles' full
+    // prefixes (it returns once the last tile's is out)
+    if (tile == 0 && wave == 0)
+        chase_prefixes<Codec>(status, (n + SG_TILE - 1) / SG_TILE, agg0, hdr);
 }
 
 // ------------------------------------------------------------------ host side

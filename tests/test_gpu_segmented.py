@@ -145,3 +145,32 @@ def test_segmented_workload_size():
     x = wl.case("int32", "sum", n, seed=21)
     h = make_heads(n, 1.0 / 1024, 22)
     check(x, "sum", True, heads=h)
+
+
+@pytest.mark.parametrize("density", [1e-5, 1e-3])
+@pytest.mark.parametrize("by_offsets", [False, True])
+def test_segmented_float_sums_repeat_bit_for_bit(density, by_offsets):
+    """Carries come from chased prefixes in an order fixed by the tile index (and head
+    tiles publish their own pair), so float32 sums give the same bits on every run;
+    the first run is also checked against the oracle."""
+    n = 300 * TILE + 7
+    x = wl.fp32_scan(n)
+    heads = make_heads(n, density, seed=int(density * 1e6) + 3)
+    xd = to_dev(x)
+    if by_offsets:
+        hh = heads.copy()
+        hh[0] = 1
+        offs = np.concatenate([np.flatnonzero(hh), [n]]).astype(np.int64)
+        od = to_dev(offs)
+        run = lambda: ps.segmented_scan(xd, "sum", False, offsets=od)
+        ref = oracle.segmented(x, "sum", True, offsets=offs)
+    else:
+        hd = to_dev(heads)
+        run = lambda: ps.segmented_scan(xd, "sum", False, heads=hd)
+        ref = oracle.segmented(x, "sum", True, heads=heads)
+    first = to_host(run())
+    ok, worst, k = oracle.fp32_sum_within_tolerance(first, ref)
+    assert ok, f"ratio {worst:.3g} at {k}"
+    for _ in range(3):
+        assert np.array_equal(bits(to_host(run())), bits(first)), "segmented sum changed between runs"
+    assert ws_error_word() == 0
