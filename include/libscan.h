@@ -291,8 +291,8 @@ ls_status ls_segmented_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t *
  *   total      NULL or 1 element: the inclusive value of element n-1 (the last
  *              segment's reduction); the identity for n == 0.
  *   ws         >= ls_segmented_workspace_bytes(n, t, op) bytes, 16-byte aligned.
- * Operators, identities and float32 behaviour as for scan_inclusive (float sums
- * may differ between runs in the last bits).  Errors: LS_ERR_INVALID_ARG for n <
+ * Operators, identities and float32 behaviour as for scan_inclusive (the same
+ * bits on every run for the same input).  Errors: LS_ERR_INVALID_ARG for n <
  * 0, NULL or misaligned buffers with n > 0, overlap (heads or total with out,
  * ws with anything), unknown enums; LS_ERR_UNSUPPORTED and LS_ERR_WORKSPACE as
  * for scan_inclusive. */
