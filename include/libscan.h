@@ -60,7 +60,8 @@ typedef enum ls_dtype { LS_INT32 = 0, LS_UINT32 = 1, LS_FLOAT32 = 2 } ls_dtype;
  *   LS_SUM     int32/uint32: addition modulo 2^32 (two's complement wrap);
  *              float32: IEEE addition; association order is the library's, so
  *              results may differ from a serial sum in the last bits ([Scan3]
- *              pitfall list) and, with the single pass, between runs.
+ *              pitfall list).  The order depends only on n and the scheme, so
+ *              they are the same bits on every run.
  *   LS_MAX     int32 signed, uint32 unsigned, float32 (a > b) ? a : b, which on a
  *              tie keeps the later element; bit-exact and run-to-run identical
  *              for data without NaN.  NaN inputs give unspecified results.
