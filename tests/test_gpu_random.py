@@ -45,7 +45,7 @@ def assert_scan(got, ref, dtype, op, seed, seg_pos=None):
         assert mism.size == 0, f"seed {seed}: {mism.size} mismatches, first at {mism[:3]}"
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(300))
 def test_random_scan(seed):
     g = np.random.default_rng(10_000 + seed)
     dtype, op = SCAN_COMBOS[g.integers(len(SCAN_COMBOS))]
@@ -62,7 +62,7 @@ def test_random_scan(seed):
     assert_scan(to_host(out), ref, dtype, op, seed)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_compaction(seed):
     g = np.random.default_rng(30_000 + seed)
     dtype = ["int32", "uint32", "float32"][g.integers(3)]
@@ -89,7 +89,7 @@ def test_random_compaction(seed):
         assert ws_error_word() == 0
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_segmented(seed):
     g = np.random.default_rng(40_000 + seed)
     combos = [("int32", "sum"), ("uint32", "max"), ("float32", "sum"), ("float32", "min"),
@@ -119,7 +119,7 @@ def test_random_segmented(seed):
         assert ws_error_word() == 0
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_sort(seed):
     g = np.random.default_rng(60_000 + seed)
     dtype = ["int32", "uint32", "float32"][g.integers(3)]
