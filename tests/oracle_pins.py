@@ -342,6 +342,49 @@ def pin_float_product(orc):
     assert orc.scan(xs, "prod", False).y[0] == 1.0
 
 
+def _exact_products(vals, starts, inclusive):
+    """Running products restarted where starts[i] is true, in exact rationals."""
+    import fractions
+    out, acc = [], fractions.Fraction(1)
+    for v, s in zip(vals, starts):
+        if s:
+            acc = fractions.Fraction(1)
+        if inclusive:
+            acc *= fractions.Fraction(v)
+            out.append(float(acc))
+        else:
+            out.append(float(acc))
+            acc *= fractions.Fraction(v)
+    return out
+
+
+def pin_float_product_segmented_and_batched(orc):
+    """Float products restart at every segment head and every row start ([Blog2]
+    §7.2; the product operator of §3.3).  Signed powers of two multiply exactly in
+    any order, so the expected prefixes are exact rationals computed here, segment
+    by segment and row by row, with nothing taken from the oracle."""
+    rng = np.random.default_rng(53)
+    n = 400
+    x = (np.ldexp(1.0, rng.integers(-3, 4, n)) * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    heads = (rng.random(n) < 0.12).astype(np.uint8)
+    heads[0] = 0  # element 0 starts a segment whether or not it is flagged
+    heads[n - 1] = 1  # a one-element segment at the end
+    starts = [i == 0 or bool(heads[i]) for i in range(n)]
+    vals = x.tolist()
+    for inc in (True, False):
+        assert orc.segmented(x, "prod", inc, heads=heads).y.tolist() == _exact_products(vals, starts, inc)
+        offs = np.concatenate([np.flatnonzero(starts), [n]]).astype(np.int64)
+        assert orc.segmented(x, "prod", inc, offsets=offs).y.tolist() == _exact_products(vals, starts, inc)
+    rows, cols = 8, 50
+    xr = x.reshape(rows, cols)
+    row_starts = [j == 0 for j in range(cols)]
+    for inc in (True, False):
+        y = orc.batched(xr, "prod", inc).y
+        assert y.shape == (rows, cols)
+        for r in range(rows):
+            assert y[r].tolist() == _exact_products(xr[r].tolist(), row_starts, inc), f"row {r}"
+
+
 # ---------------------------------------------------------------- segmented scan
 
 def _brute_segmented(bits, heads, dtype, op, inclusive):
@@ -363,9 +406,11 @@ def pin_segmented_special_cases(orc):
     on every element leaves x (inclusive) or the identity (exclusive)."""
     rng = np.random.default_rng(41)
     for dtype, op in (("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("uint32", "affine"),
-                      ("int32", "prod"), ("float32", "max"), ("float32", "min")):
+                      ("int32", "prod"), ("float32", "max"), ("float32", "min"), ("float32", "prod")):
         rows, cols = 7, 13
         x = wl_case(rng, dtype, op, rows * cols)
+        if (dtype, op) == ("float32", "prod"):
+            x = (x / np.float32(16)).astype(np.float32)  # keep the products of a row in range
         heads = np.zeros(rows * cols, np.uint8)
         heads[::cols] = 1
         for inc in (True, False):
@@ -375,8 +420,12 @@ def pin_segmented_special_cases(orc):
             one = orc.segmented(x, op, inc, heads=np.zeros(rows * cols, np.uint8)).y
             assert _bits(one) == _bits(orc.scan(x, op, inc).y)
         every = orc.segmented(x, op, True, heads=np.ones(rows * cols, np.uint8)).y
-        assert _bits(every) == _bits(x)
         ex = orc.segmented(x, op, False, heads=np.full(rows * cols, 7, np.uint8)).y
+        if (dtype, op) == ("float32", "prod"):  # float products are carried in double
+            assert every.tolist() == [float(v) for v in x.tolist()]
+            assert all(v == 1.0 for v in ex.tolist())
+            continue
+        assert _bits(every) == _bits(x)
         want = _ident(dtype, op) if dtype != "float32" else {"max": 0xFF800000, "min": 0x7F800000}[op]
         assert all(b == want for b in _bits(ex))
 

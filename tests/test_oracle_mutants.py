@@ -68,6 +68,19 @@ MUTANTS = [
     ("seg_minmax_tie_lost", "            acc = is_min ? fmin_right(acc, x[i]) : fmax_right(acc, x[i]);\n            y[i] = acc;",
      "            acc = is_min ? fmin_right(x[i], acc) : fmax_right(x[i], acc);\n            y[i] = acc;"),
     ("offsets_drop_last_segment", "    for (int64_t k = 0; k < nseg; ++k) {", "    for (int64_t k = 0; k < nseg - 1; ++k) {"),
+    ("seg_f32_prod_no_restart",
+     "        if (i == 0 || heads[i] != 0)\n            acc = 1.0;\n",
+     ""),
+    ("seg_f32_prod_restart_zero",
+     "        if (i == 0 || heads[i] != 0)\n            acc = 1.0;\n",
+     "        if (i == 0 || heads[i] != 0)\n            acc = 0.0;\n"),
+    ("seg_f32_prod_exclusive_is_inclusive",
+     "            y[i] = acc;\n            acc *= (double)x[i];",
+     "            acc *= (double)x[i];\n            y[i] = acc;"),
+    ("batched_f32_prod_row_stride", "oracle_scan_f32_prod(x + r * cols, y + r * cols,",
+     "oracle_scan_f32_prod(x + r, y + r * cols,"),
+    ("batched_f32_prod_carry", "oracle_scan_f32_prod(x + r * cols, y + r * cols,",
+     "oracle_scan_f32_prod(x, y + r * cols,"),
     ("f32_prod_exclusive_dropped_term", "            y[i] = acc;\n            acc *= v;",
      "            acc *= v;\n            y[i] = acc;"),
 ]
