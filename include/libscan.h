@@ -190,6 +190,27 @@ ls_status ls_scan_ex_workspace_bytes(int64_t n, ls_dtype t, ls_op op, ls_scheme 
 ls_status scan_ex(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, int exclusive,
                   ls_scheme scheme, void *total, void *ws, size_t ws_bytes, void *stream);
 
+/* Largest n that scan_noalloc accepts. */
+#define LS_SCAN_NOALLOC_MAX_N 402653184LL
+
+/* scan_inclusive / scan_exclusive for callers that cannot allocate device memory
+ * at the point of the call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace: the library keeps a
+ * fixed 4 MiB array in device memory per GPU (held until the process ends) and
+ * uses it as the single-pass scan's workspace; the call itself allocates and frees
+ * nothing.  The first call on a device looks the array up and enqueues its zero
+ * fill on `stream` ahead of the scan.
+ *   exclusive  nonzero: exclusive scan; zero: inclusive.
+ *   n          0 <= n <= LS_SCAN_NOALLOC_MAX_N; a larger n returns
+ *              LS_ERR_WORKSPACE and enqueues nothing.
+ * Other arguments, results and errors as for scan_inclusive / scan_exclusive.
+ * Every call on one GPU shares that GPU's array: calls whose execution may
+ * overlap on one GPU (on different streams without an ordering between them, or
+ * from several host threads) race and give wrong results.  Calls on one stream,
+ * or ordered by events, are safe. */
+ls_status scan_noalloc(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                       void *total, void *stream);
+
 /* Workspace size for compact_if (same rules as ls_scan_workspace_bytes). */
 ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t *bytes);
 

@@ -24,7 +24,7 @@ __all__ = [
     "compact_if", "batched_row_scan", "workspace_for", "scan_ex", "ls_scan_ex_workspace_bytes",
     "batched_row_scan_ex", "radix_sort", "ls_radix_sort_workspace_bytes", "compact_flags",
     "select_indices_if", "select_indices_flags",
-    "segmented_scan", "ls_segmented_workspace_bytes",
+    "segmented_scan", "ls_segmented_workspace_bytes", "scan_noalloc", "SCAN_NOALLOC_MAX_N",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,8 @@ BLOCK_SCAN_CODES = {"wave_dpp": 0, "hillis_steele": 1, "hillis_steele_double": 2
 _TORCH_DTYPES = {torch.int32: "int32", torch.float32: "float32"}
 if hasattr(torch, "uint32"):
     _TORCH_DTYPES[torch.uint32] = "uint32"
+
+SCAN_NOALLOC_MAX_N = 402653184  # LS_SCAN_NOALLOC_MAX_N
 
 _lock = threading.Lock()
 _lib = None
@@ -107,6 +109,8 @@ def load_library():
         lib.ls_radix_sort_workspace_bytes.restype = I
         lib.radix_sort.argtypes = [P, P, P, P, I64, I, P, SZ, P]
         lib.radix_sort.restype = I
+        lib.scan_noalloc.argtypes = [P, P, I64, I, I, I, P, P]
+        lib.scan_noalloc.restype = I
         lib.compact_if.argtypes = [P, P, P, I64, I, I, U32, P, SZ, P]
         lib.compact_if.restype = I
         lib.batched_row_scan.argtypes = [P, P, I64, I64, I, I, I, P]
@@ -269,6 +273,30 @@ def scan_exclusive(x: torch.Tensor, op: str = "sum", out: torch.Tensor | None = 
                    total: torch.Tensor | None = None) -> torch.Tensor:
     """out[0] = identity, out[i] = x[0] (+) ... (+) x[i-1]."""
     return _scan("scan_exclusive", x, op, out, total)
+
+
+def scan_noalloc(x: torch.Tensor, op: str = "sum", exclusive: bool = False,
+                 out: torch.Tensor | None = None, total: torch.Tensor | None = None) -> torch.Tensor:
+    """The scan on the library's fixed per-GPU workspace (no workspace argument, no
+    allocation inside the call; n <= LS_SCAN_NOALLOC_MAX_N).  Calls that may overlap
+    on one GPU race: keep them on one stream.  With out and total given, this
+    function allocates nothing either."""
+    lib = load_library()
+    _require_gpu(x, out, total)
+    if not x.is_contiguous():
+        raise ValueError("libscan: input must be contiguous")
+    dt = _dtype_of(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
+        raise ValueError("libscan: out must be a contiguous tensor like the input")
+    if total is not None and (total.dtype != x.dtype or total.numel() < 1):
+        raise ValueError("libscan: total must hold one element of the input dtype")
+    _, sh = _stream_handle(x.device)
+    st = lib.scan_noalloc(_ptr(x), _ptr(out), x.numel(), DTYPE_CODES[dt], OP_CODES[op],
+                          1 if exclusive else 0, _ptr(total), sh)
+    _check(st, "scan_noalloc")
+    return out
 
 
 def scan_ex(x: torch.Tensor, op: str = "sum", inclusive: bool = True,

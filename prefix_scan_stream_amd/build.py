@@ -35,7 +35,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-paramet
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["ls_scan.hip", "ls_compact.hip", "ls_batched.hip", "ls_sort.hip", "ls_segmented.hip",
-           "ls_api.cpp"]
+           "ls_noalloc.hip", "ls_api.cpp"]
 
 
 def exported_symbols() -> list[str]:

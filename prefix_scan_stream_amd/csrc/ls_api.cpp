@@ -48,8 +48,11 @@ ls_status check_ws(const void* ws, size_t ws_bytes, size_t need)
     return LS_OK;
 }
 
+// noalloc: ws / ws_bytes are ignored and the library's fixed per-device workspace
+// is used (looked up once the arguments have passed their checks).
 ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, void* total,
-                      void* ws, size_t ws_bytes, void* stream, bool inclusive, ls_scheme scheme)
+                      void* ws, size_t ws_bytes, void* stream, bool inclusive, ls_scheme scheme,
+                      bool noalloc = false)
 {
     if (!size_ok(n) || !valid_dtype(t) || !valid_op(op) || !valid_scheme(scheme))
         return LS_ERR_INVALID_ARG;
@@ -67,6 +70,13 @@ ls_status scan_common(const void* in, void* out, int64_t n, ls_dtype t, ls_op op
     if (op_unsupported(t, op))
         return LS_ERR_UNSUPPORTED;
     const size_t need = ls::scan_workspace_bytes(n, int(scheme));
+    if (noalloc) {
+        if (n > LS_SCAN_NOALLOC_MAX_N || need > ls::NOALLOC_SCRATCH_BYTES)
+            return LS_ERR_WORKSPACE;
+        if (ls::noalloc_scratch(reinterpret_cast<hipStream_t>(stream), &ws) != hipSuccess)
+            return LS_ERR_HIP;
+        ws_bytes = ls::NOALLOC_SCRATCH_BYTES;
+    }
     ls_status st = check_ws(ws, ws_bytes, need);
     if (st != LS_OK)
         return st;
@@ -220,6 +230,13 @@ ls_status scan_ex(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, in
                   ls_scheme scheme, void* total, void* ws, size_t ws_bytes, void* stream)
 {
     return scan_common(in, out, n, t, op, total, ws, ws_bytes, stream, exclusive == 0, scheme);
+}
+
+ls_status scan_noalloc(const void* in, void* out, int64_t n, ls_dtype t, ls_op op, int exclusive,
+                       void* total, void* stream)
+{
+    return scan_common(in, out, n, t, op, total, nullptr, 0, stream, exclusive == 0, LS_SCHEME_SINGLE_PASS,
+                       true);
 }
 
 ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t* bytes)

@@ -124,6 +124,27 @@ def test_scan_validation(lib, fn):
     assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=XOR, ws=None) == UNS
 
 
+def test_noalloc_scan_validation(lib):
+    """scan_noalloc checks its arguments like the scans (on the host, before the
+    library's fixed workspace is looked up) and refuses n above its maximum."""
+    f = lib.scan_noalloc
+    assert f(A_IN, A_OUT, -1, INT32, SUM, 1, None, None) == INV
+    assert f(None, A_OUT, 10, INT32, SUM, 1, None, None) == INV
+    assert f(A_IN, A_OUT + 2, 10, INT32, SUM, 0, None, None) == INV
+    assert f(A_IN, A_IN + 4, 10, INT32, SUM, 0, None, None) == INV
+    assert f(A_IN, A_OUT, 10, 3, SUM, 0, None, None) == INV
+    assert f(A_IN, A_OUT, 10, F32, XOR, 0, None, None) == UNS
+    assert f(A_IN, A_OUT, 10, INT32, SUM, 0, A_OUT + 8, None) == INV
+    far = A_IN - (1 << 40)  # far enough below `in` that the large sizes do not overlap it
+    assert f(A_IN, far, ps.SCAN_NOALLOC_MAX_N + 1, INT32, SUM, 1, None, None) == WS
+    assert f(A_IN, far, 1 << 36, F32, MAX, 0, None, None) == WS
+    # the fixed 4 MiB workspace holds the single pass's status words at the maximum n
+    for t, op in ((INT32, SUM), (F32, SUM), (UINT32, AFFINE)):
+        need = ctypes.c_size_t(0)
+        assert lib.ls_scan_workspace_bytes(ps.SCAN_NOALLOC_MAX_N, t, op, ctypes.byref(need)) == 0
+        assert need.value <= 4 << 20
+
+
 def test_extended_entry_points_validation(lib):
     sz = ctypes.c_size_t(0)
     for scheme in range(4):
