@@ -13,8 +13,10 @@ library launches on give the time.  The JSON line also carries:
   cpu_baseline  the serial CPU oracle timed on this host on the same input;
   legs          the other workloads: fused compaction (N = 2^27 at 1/50/99 %),
                 float32 sum and int32 max scans (N = 2^26), the two batched row
-                shapes, the 2^20 scan (latency-bound), and a plain device copy of
-                the headline byte count (a practical bandwidth ceiling).
+                shapes, the 2^20 scan (latency-bound), and the plain read / write /
+                copy kernels of libls_ceiling.so over the headline's bytes (the
+                practical bandwidth ceilings).  Each leg reports its mean, median and
+                minimum time per call.
 Only rank 0 of one GPU exists here; --gpus above 1 is refused.
 """
 from __future__ import annotations
@@ -35,7 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
-ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "copy", "schemes",
+ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "ceiling", "schemes",
             "blockscans", "sort", "select", "ops", "segmented")
 DEFAULT_LEGS = ALL_LEGS
 
@@ -72,24 +74,79 @@ def read_traffic():
 
 
 class Timer:
-    """HIP events recorded on the current (library) stream."""
+    """HIP events recorded on the current stream, the one the library launches on.
+    A run times `steps` calls between two events (the mean it returns), then
+    repeats the same batch REPEATS more times for the spread: the median and
+    minimum of the batch means.  (An event between every call would add a few
+    microseconds to each.)"""
+
+    REPEATS = 5
 
     def __init__(self, torch):
         self.torch = torch
-        self.a = torch.cuda.Event(enable_timing=True)
-        self.b = torch.cuda.Event(enable_timing=True)
+        self.batches = []  # batch means (ms per step) of the last run
 
-    def run(self, fn, steps: int, warmup: int) -> float:
+    def _batch(self, fn, steps: int) -> float:
         torch = self.torch
-        for i in range(warmup):
-            fn(i)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        self.a.record()
+        a.record()
         for i in range(steps):
             fn(i)
-        self.b.record()
+        b.record()
         torch.cuda.synchronize()
-        return self.a.elapsed_time(self.b) / steps  # ms per step
+        return a.elapsed_time(b) / steps
+
+    def run(self, fn, steps: int, warmup: int) -> float:
+        for i in range(warmup):
+            fn(i)
+        ms = self._batch(fn, steps)
+        self.batches = [ms] + [self._batch(fn, steps) for _ in range(self.REPEATS)]
+        return ms  # ms per step of the first batch
+
+    def spread(self) -> dict:
+        """Median and minimum over the batches of the last run (us per call)."""
+        t = sorted(self.batches)
+        return {"us_median": round(1e3 * t[len(t) // 2], 2), "us_min": round(1e3 * t[0], 2)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.partition(":")[2].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Ceilings:
+    """The plain read / write / copy kernels of libls_ceiling.so (include/ls_ceiling.h)."""
+
+    def __init__(self):
+        import ctypes
+        path = os.path.join(ROOT, "prefix_scan_stream_amd", "libls_ceiling.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} not found; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        lib.ls_ceiling_read.argtypes = [P, SZ, P, I, P]
+        lib.ls_ceiling_write.argtypes = [P, SZ, I, P]
+        lib.ls_ceiling_copy.argtypes = [P, P, SZ, I, P]
+        self.lib = lib
+
+    def call(self, kind, torch, a, b, sink, bpc):
+        s = torch.cuda.current_stream().cuda_stream
+        if kind == "read":
+            st = self.lib.ls_ceiling_read(a.data_ptr(), a.numel() * a.element_size(), sink.data_ptr(), bpc, s)
+        elif kind == "write":
+            st = self.lib.ls_ceiling_write(b.data_ptr(), b.numel() * b.element_size(), bpc, s)
+        else:
+            st = self.lib.ls_ceiling_copy(a.data_ptr(), b.data_ptr(), a.numel() * a.element_size(), bpc, s)
+        if st != 0:
+            raise RuntimeError(f"ls_ceiling_{kind} returned {st}")
 
 
 def main():
@@ -142,7 +199,7 @@ def main():
         achieved = algo_bytes / (ms * 1e-3) / 1e9
         traffic = read_traffic()
         headline = dict(n=n, ms=ms, gelem=gelem, achieved=achieved, algo_bytes=algo_bytes,
-                        traffic=traffic)
+                        traffic=traffic, **timer.spread())
         log(f"scan: {ms * 1e3:.1f} us/step, {gelem:.1f} Gelem/s, {achieved:.0f} GB/s")
         cpu = None
         if not args.no_cpu_baseline:
@@ -155,7 +212,8 @@ def main():
             cpu = {"value": round(n / (t1 - t0) / 1e9, 4), "unit": "Gelem/s", "cores": 1,
                    "kind": "oracle",
                    "sample": f"the whole workload once: int32 exclusive sum of N={n} "
-                             f"({t1 - t0:.2f} s on 1 of {len(os.sched_getaffinity(0))} host cores)"}
+                             f"({t1 - t0:.2f} s on 1 of {len(os.sched_getaffinity(0))} host cores)",
+                   "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
             headline["sample_check"] = ok
             if not ok:
                 log("scan: SAMPLED OUTPUT DISAGREES WITH THE ORACLE")
@@ -171,7 +229,7 @@ def main():
         x = to_dev(wl.small_scan())
         out = torch.empty_like(x)
         ms = timer.run(lambda i: ps.scan_exclusive(x, "sum", out=out), max(K, 50), W)
-        result_legs["small_scan_i32_excl_2e20"] = {"us": round(ms * 1e3, 2),
+        result_legs["small_scan_i32_excl_2e20"] = {"us": round(ms * 1e3, 2), **timer.spread(),
                                                    "gelem_s": round(x.numel() / ms / 1e6, 1),
                                                    "note": "cache-resident, latency-bound"}
         log(f"small: {ms * 1e3:.2f} us")
@@ -180,8 +238,8 @@ def main():
         outs = [torch.empty_like(t) for t in xs]
         ms = timer.run(lambda i: fn(xs[i % len(xs)], outs[i % len(outs)]), K, W)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        result_legs[name] = {"us": round(ms * 1e3, 1), "gelem_s": round(elems / ms / 1e6, 1),
-                             "algo_gbs": round(gbs, 1),
+        result_legs[name] = {"us": round(ms * 1e3, 1), **timer.spread(),
+                             "gelem_s": round(elems / ms / 1e6, 1), "algo_gbs": round(gbs, 1),
                              "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
         log(f"{name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
 
@@ -302,15 +360,26 @@ def main():
                                  "bytes_moved_per_key": 4 * per_pass}
             log(f"{name}: {ms * 1e3:.1f} us, {n / ms / 1e6:.2f} Gkeys/s")
         del keys, vals, ok_, ov_
-    if "copy" in legs:
+    if "ceiling" in legs:
+        # plain read / write / copy kernels over the headline's bytes (1 GiB each way):
+        # the practical ceilings, best over three grid sizes
         n = wl.SIZES["big_scan"]
         a = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)
         b = torch.empty_like(a)
-        ms = timer.run(lambda i: b.copy_(a), K, W)
-        gbs = 8 * n / (ms * 1e-3) / 1e9
-        result_legs["device_copy_1GiB"] = {"us": round(ms * 1e3, 1), "gbs": round(gbs, 1),
-                                           "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"copy: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        ce = Ceilings()
+        for kind, nbytes in (("read", 4 * n), ("write", 4 * n), ("copy", 8 * n)):
+            best = None
+            for bpc in (4, 8, 16):
+                ms = timer.run(lambda i, k=kind, bpc=bpc: ce.call(k, torch, a, b, sink, bpc), K, W)
+                if best is None or ms < best[0]:
+                    best = (ms, bpc, timer.spread())
+            ms, bpc, spread = best
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            result_legs[f"ceiling_{kind}_1GiB"] = {"us": round(ms * 1e3, 1), **spread, "gbs": round(gbs, 1),
+                                                  "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                                  "blocks_per_cu": bpc}
+            log(f"ceiling {kind}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({bpc} blocks per CU)")
         del a, b
 
     if headline is None:
@@ -336,6 +405,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": h["traffic"]},
+        "step_us": {"mean": round(h["ms"] * 1e3, 2), "median": h["us_median"], "min": h["us_min"]},
         "cpu_baseline": h["cpu"],
         "sample_check": h.get("sample_check"),
         "legs": result_legs,

@@ -31,6 +31,29 @@
  *     run a slower path.
  *   - Concurrent calls must use distinct workspaces; calls that share a
  *     workspace on different streams race.
+ *
+ * Workspaces
+ *   The scans, segmented scans, compactions and the radix sort take a caller's
+ *   device workspace of at least the size that the matching *_workspace_bytes
+ *   query returns.  Inside a call, tiles hand their results on through tile
+ *   status words in the workspace ([Scan3] 四: blocks passing their totals on
+ *   through flags in global memory; [SIMT3] 5.1: flags published with fences).
+ *   - Status workspaces, of the single-pass scans (scan_inclusive,
+ *     scan_exclusive, scan_ex with a single-pass scheme), segmented scans and
+ *     compactions: zero-filled once before first use, by ls_workspace_init (or
+ *     any zero fill of the whole buffer).  Every call leaves the workspace ready
+ *     for the next, so calls enqueue no clearing work of their own.  Between
+ *     calls its contents must not change, and it must serve no other purpose: a
+ *     status workspace used by a radix sort or a three-phase scan_ex, or written
+ *     in any other way, must be initialised again.  Apart from that it may serve
+ *     any sequence of these calls, of any sizes it is large enough for.
+ *   - The radix sort and the three-phase scan_ex schemes use their workspace as
+ *     plain scratch: its contents on entry do not matter.  (For the sort's error
+ *     word to be meaningful, initialise its workspace once.)
+ *   Each wait for another tile is bounded: after about one second without
+ *   progress it gives up, the call's output is then incomplete, and the
+ *   workspace records the fact; ls_workspace_check reports it.  In a correct run
+ *   no wait lasts more than microseconds.
  */
 #ifndef LIBSCAN_H
 #define LIBSCAN_H
@@ -42,14 +65,20 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 4
+#define LS_ABI_VERSION 5
+
+/* Largest element count of the scans, segmented scans and the radix sort (tile ids
+ * are 32 bits), and of the compaction family (its counts travel in 36 bits). */
+#define LS_MAX_N (1LL << 40)
+#define LS_COMPACT_MAX_N ((1LL << 36) - 1)
 
 typedef enum ls_status {
     LS_OK = 0,
     LS_ERR_INVALID_ARG = 1, /* bad size, NULL, alignment, enum value, or overlap */
     LS_ERR_UNSUPPORTED = 2, /* an operator not defined for the element type (see ls_op) */
     LS_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the size query returned */
-    LS_ERR_HIP = 4          /* the HIP runtime reported an error when enqueuing */
+    LS_ERR_HIP = 4,         /* the HIP runtime reported an error when enqueuing */
+    LS_ERR_INCOMPLETE = 5   /* ls_workspace_check: a call on the workspace gave up a wait */
 } ls_status;
 
 /* Element types.  All are 32 bits wide. */
@@ -152,6 +181,28 @@ int ls_abi_version(void);
 /* A static, human-readable string for a status code (never NULL). */
 const char *ls_status_string(ls_status s);
 
+/* Zero-fills a workspace before its first use (or after ls_workspace_check
+ * reported LS_ERR_INCOMPLETE): a fill kernel enqueued on `stream` (so the call
+ * may be captured in a graph).
+ *   ws        device workspace, 16-byte aligned.
+ *   ws_bytes  its size: at least 256 and a multiple of 16.
+ * Errors: LS_ERR_INVALID_ARG for NULL, misaligned or too small a workspace or a
+ * size that is not a multiple of 16; LS_ERR_HIP when the launch fails. */
+ls_status ls_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Reports whether a call on this workspace gave up a bounded wait since the
+ * workspace was last initialised.  Unlike the other entry points this call
+ * waits: it copies the workspace's error word to the host on `stream` and
+ * synchronises the stream.
+ *   flags (host, out, nullable): the error bits (1 = a wait gave up; 2 = a tile id
+ *         beyond the call's tiles was handed out, i.e. the workspace was not
+ *         initialised or calls sharing it overlapped).
+ * Returns LS_OK when no bit is set, LS_ERR_INCOMPLETE when one is (the outputs of
+ * the calls since the last initialisation may be incomplete; initialise the
+ * workspace again before further use), LS_ERR_INVALID_ARG for a NULL or
+ * misaligned ws, LS_ERR_HIP when the copy fails. */
+ls_status ls_workspace_check(const void *ws, uint32_t *flags, void *stream);
+
 /* Workspace size for scan_inclusive / scan_exclusive.
  *   bytes (host, out): size of the device workspace a call with these arguments
  *   needs (never 0).  Errors: LS_ERR_INVALID_ARG for n < 0, bytes == NULL or an
@@ -163,14 +214,15 @@ ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t *bytes
  *
  *   in, out   n elements of type t.  out == in (exact aliasing, in place) is
  *             allowed; any other overlap is LS_ERR_INVALID_ARG.
- *   n         element count, 0 <= n.  n == 0 writes only *total (= identity).
+ *   n         element count, 0 <= n <= LS_MAX_N.  n == 0 writes only *total
+ *             (= identity).
  *   t, op     element type and operator (see ls_op).
  *   total     nullable; receives one element: the reduction of all n inputs,
  *             i.e. the value that no exclusive cell holds ([Scan3] 一).
  *   ws        device workspace of ws_bytes >= ls_scan_workspace_bytes(...),
  *             16-byte aligned (else LS_ERR_INVALID_ARG), not overlapping any
- *             other argument.  Its contents on entry do not matter; the call
- *             re-initialises what it uses.
+ *             other argument, zero-filled before its first use (see
+ *             "Workspaces" above).
  *   stream    hipStream_t as void*, or NULL.
  * One pass over the data: each element is read once and written once. */
 ls_status scan_inclusive(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, void *total,
@@ -221,6 +273,7 @@ ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t *bytes);
  *   in             n elements of type t.
  *   out            capacity n elements; must not overlap `in`.  Cells at index
  *                  >= *count are not written.
+ *   n              0 <= n <= LS_COMPACT_MAX_N.
  *   count          device int64_t, written with the number of kept elements
  *                  (0 when n == 0).  Must not overlap in/out.
  *   threshold_bits the 32-bit pattern of the threshold in type t.

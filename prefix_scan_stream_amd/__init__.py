@@ -7,7 +7,15 @@ the library's HIP kernels; there is no other implementation behind these names,
 and importing or calling them fails loudly when libscan.so is missing.
 
 PyTorch supplies device memory and streams only.  Workspaces are cached per
-(device, stream) and grown on demand.
+(device, stream), zero-filled by the library once when they are made, and grown
+on demand; a workspace that a larger one replaces is kept, not freed, because a
+HIP graph captured earlier may still use it (release_workspaces() frees them).
+
+Checked mode (set_checked(True), or LIBSCAN_CHECKED=1 in the environment) reads
+the workspace's error word after every call that uses one -- which waits for the
+stream -- and raises LibscanError(LS_ERR_INCOMPLETE) when a bounded wait inside
+the call gave up, re-initialising the workspace.  It is off by default so that
+calls stay asynchronous and can be captured in graphs.
 """
 from __future__ import annotations
 
@@ -25,12 +33,14 @@ __all__ = [
     "batched_row_scan_ex", "radix_sort", "ls_radix_sort_workspace_bytes", "compact_flags",
     "select_indices_if", "select_indices_flags",
     "segmented_scan", "ls_segmented_workspace_bytes", "scan_noalloc", "SCAN_NOALLOC_MAX_N",
+    "ls_workspace_init", "ls_workspace_check", "set_checked", "workspace_error_flags",
+    "release_workspaces",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libscan.so")
 
-LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = range(5)
+LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP, LS_ERR_INCOMPLETE = range(6)
 DTYPE_CODES = {"int32": 0, "uint32": 1, "float32": 2}
 OP_CODES = {"sum": 0, "max": 1, "xor": 2, "min": 3, "and": 4, "or": 5, "prod": 6, "affine": 7}
 CMP_CODES = {"lt": 0, "le": 1, "gt": 2, "ge": 3, "eq": 4, "ne": 5}
@@ -45,7 +55,8 @@ SCAN_NOALLOC_MAX_N = 402653184  # LS_SCAN_NOALLOC_MAX_N
 
 _lock = threading.Lock()
 _lib = None
-ABI_VERSION = 4  # the libscan.h version this binding marshals for
+ABI_VERSION = 5  # the libscan.h version this binding marshals for
+_checked = os.environ.get("LIBSCAN_CHECKED", "0") not in ("", "0")
 
 
 class LibscanError(RuntimeError):
@@ -79,6 +90,10 @@ def load_library():
                               f"needs {ABI_VERSION}; rebuild with `python -m prefix_scan_stream_amd.build`")
         lib.ls_status_string.argtypes = [I]
         lib.ls_status_string.restype = ctypes.c_char_p
+        lib.ls_workspace_init.argtypes = [P, SZ, P]
+        lib.ls_workspace_init.restype = I
+        lib.ls_workspace_check.argtypes = [P, ctypes.POINTER(U32), P]
+        lib.ls_workspace_check.restype = I
         lib.ls_scan_workspace_bytes.argtypes = [I64, I, I, ctypes.POINTER(SZ)]
         lib.ls_scan_workspace_bytes.restype = I
         lib.ls_compact_workspace_bytes.argtypes = [I64, I, ctypes.POINTER(SZ)]
@@ -156,18 +171,82 @@ def ls_compact_workspace_bytes(n: int, dtype: str) -> int:
 
 # ------------------------------------------------------------ workspaces
 
-_ws_cache: dict = {}
+_ws_cache: dict = {}    # (device index, stream handle) -> the uint8 workspace in use
+_ws_retired: list = []  # workspaces replaced by larger ones, kept for graphs that captured them
 
 
-def workspace_for(device: torch.device, stream: torch.cuda.Stream, nbytes: int) -> torch.Tensor:
-    """A cached uint8 device buffer of at least nbytes for (device, stream)."""
-    key = (device.index, stream.cuda_stream)
+def set_checked(on: bool = True) -> None:
+    """Checked mode: after each call that uses a workspace, wait for the stream and
+    raise LibscanError(LS_ERR_INCOMPLETE) if a bounded wait in the call gave up."""
+    global _checked
+    _checked = bool(on)
+
+
+def ls_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    """Zero-fill a uint8 device workspace (before first use) on `stream` (default:
+    the current stream)."""
+    _require_gpu(ws)
+    s = stream if stream is not None else torch.cuda.current_stream(ws.device)
+    _check(load_library().ls_workspace_init(_ptr(ws), ws.numel(), ctypes.c_void_p(s.cuda_stream)),
+           "ls_workspace_init")
+
+
+def ls_workspace_check(ws: torch.Tensor, stream=None) -> int:
+    """The workspace's error bits (0: no call on it gave up a wait since it was last
+    initialised).  Waits for `stream` (default: the current stream)."""
+    _require_gpu(ws)
+    s = stream if stream is not None else torch.cuda.current_stream(ws.device)
+    flags = ctypes.c_uint32(0)
+    st = load_library().ls_workspace_check(_ptr(ws), ctypes.byref(flags), ctypes.c_void_p(s.cuda_stream))
+    if st not in (LS_OK, LS_ERR_INCOMPLETE):
+        _check(st, "ls_workspace_check")
+    return flags.value
+
+
+def workspace_for(device: torch.device, stream: torch.cuda.Stream, nbytes: int,
+                  kind: str = "status") -> torch.Tensor:
+    """The cached, initialised uint8 workspace of (device, stream, kind), of at least
+    nbytes.  Kinds keep apart what the C ABI requires to be apart: "status" for the
+    single-pass scans, segmented scans and compactions (tile status words that must
+    never be overwritten with other data), "sort" for the radix sort and "phases"
+    for the three-phase scan_ex schemes (plain scratch)."""
+    key = (device.index, stream.cuda_stream, kind)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        size = max(nbytes, 1 << 16)
-        buf = torch.empty(size, dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
+        size = (max(nbytes, 1 << 16) + 255) & ~255
+        new = torch.empty(size, dtype=torch.uint8, device=device)
+        ls_workspace_init(new, stream)
+        if buf is not None:
+            _ws_retired.append(buf)
+        _ws_cache[key] = new
+        buf = new
     return buf
+
+
+def workspace_error_flags(device=None, stream=None) -> int:
+    """Error bits of the cached workspace of (device, stream) (defaults: cuda:0's
+    current stream); 0 when there is none yet.  Waits for the stream."""
+    device = torch.device(device if device is not None else "cuda:0")
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    buf = _ws_cache.get((device.index, s.cuda_stream, "status"))
+    return 0 if buf is None else ls_workspace_check(buf, s)
+
+
+def release_workspaces() -> None:
+    """Drop every cached and retired workspace (no graph that used one may be
+    replayed afterwards)."""
+    _ws_cache.clear()
+    _ws_retired.clear()
+
+
+def _after_call(ws: torch.Tensor, stream, where: str) -> None:
+    """Checked mode: report a call whose bounded wait gave up."""
+    if not _checked:
+        return
+    flags = ls_workspace_check(ws, stream)
+    if flags:
+        ls_workspace_init(ws, stream)
+        raise LibscanError(LS_ERR_INCOMPLETE, f"{where} (workspace error bits {flags:#x})")
 
 
 def _dtype_of(x: torch.Tensor) -> str:
@@ -213,6 +292,7 @@ def _scan(name: str, x: torch.Tensor, op: str, out, total):
     st = getattr(lib, name)(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], _ptr(total),
                             _ptr(ws), ws.numel(), sh)
     _check(st, name)
+    _after_call(ws, stream, name)
     return out
 
 
@@ -252,6 +332,7 @@ def segmented_scan(x: torch.Tensor, op: str = "sum", exclusive: bool = False,
         st = lib.segmented_scan(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], excl, _ptr(heads),
                                 _ptr(total), _ptr(ws), ws.numel(), sh)
         _check(st, "segmented_scan")
+        _after_call(ws, stream, "segmented_scan")
     else:
         if offsets.dtype != torch.int64 or not offsets.is_contiguous() or offsets.numel() < 1:
             raise ValueError("libscan: offsets must be a contiguous int64 tensor of nseg + 1 entries")
@@ -259,6 +340,7 @@ def segmented_scan(x: torch.Tensor, op: str = "sum", exclusive: bool = False,
                                         _ptr(offsets), offsets.numel() - 1, _ptr(total), _ptr(ws),
                                         ws.numel(), sh)
         _check(st, "segmented_scan_offsets")
+        _after_call(ws, stream, "segmented_scan_offsets")
     return out
 
 
@@ -318,10 +400,13 @@ def scan_ex(x: torch.Tensor, op: str = "sum", inclusive: bool = True,
     n = x.numel()
     stream, sh = _stream_handle(x.device)
     need = ls_scan_ex_workspace_bytes(n, dt, op, scheme)
-    ws = workspace_for(x.device, stream, need)
+    phases = scheme in ("reduce_then_scan", "scan_then_propagate")
+    ws = workspace_for(x.device, stream, need, "phases" if phases else "status")
     st = lib.scan_ex(_ptr(x), _ptr(out), n, DTYPE_CODES[dt], OP_CODES[op], 0 if inclusive else 1,
                      SCHEME_CODES[scheme], _ptr(total), _ptr(ws), ws.numel(), sh)
     _check(st, "scan_ex")
+    if not phases:  # the three-phase schemes never wait, and keep no error word
+        _after_call(ws, stream, "scan_ex")
     return out
 
 
@@ -350,6 +435,7 @@ def compact_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | None = 
     st = lib.compact_if(_ptr(x), _ptr(out), _ptr(count), n, DTYPE_CODES[dt], CMP_CODES[cmp],
                         thr_bits, _ptr(ws), ws.numel(), sh)
     _check(st, "compact_if")
+    _after_call(ws, stream, "compact_if")
     return out, count
 
 
@@ -391,6 +477,7 @@ def compact_flags(x: torch.Tensor, flags: torch.Tensor, out: torch.Tensor | None
     ws = workspace_for(x.device, stream, ls_compact_workspace_bytes(n, "uint32"))
     st = lib.compact_flags(_ptr(x), _ptr(flags), _ptr(out), _ptr(count), n, _ptr(ws), ws.numel(), sh)
     _check(st, "compact_flags")
+    _after_call(ws, stream, "compact_flags")
     return out, count
 
 
@@ -412,6 +499,7 @@ def select_indices_if(x: torch.Tensor, cmp: str, threshold, out: torch.Tensor | 
     st = lib.select_indices_if(_ptr(x), _ptr(out), _ptr(count), n, DTYPE_CODES[dt], CMP_CODES[cmp],
                                _threshold_bits(dt, threshold), _ptr(ws), ws.numel(), sh)
     _check(st, "select_indices_if")
+    _after_call(ws, stream, "select_indices_if")
     return out, count
 
 
@@ -429,6 +517,7 @@ def select_indices_flags(flags: torch.Tensor, out: torch.Tensor | None = None,
     ws = workspace_for(flags.device, stream, ls_compact_workspace_bytes(n, "uint32"))
     st = lib.select_indices_flags(_ptr(flags), _ptr(out), _ptr(count), n, _ptr(ws), ws.numel(), sh)
     _check(st, "select_indices_flags")
+    _after_call(ws, stream, "select_indices_flags")
     return out, count
 
 
@@ -495,9 +584,10 @@ def radix_sort(keys: torch.Tensor, values: torch.Tensor | None = None,
         out_values = torch.empty_like(values)
     stream, sh = _stream_handle(keys.device)
     need = ls_radix_sort_workspace_bytes(n, dt, values is not None)
-    ws = workspace_for(keys.device, stream, need)
+    ws = workspace_for(keys.device, stream, need, "sort")
     st = lib.radix_sort(_ptr(keys), _ptr(out_keys), _ptr(values), _ptr(out_values), n, DTYPE_CODES[dt],
                         _ptr(ws), ws.numel(), sh)
     _check(st, "radix_sort")
+    _after_call(ws, stream, "radix_sort")
     return out_keys, (out_values if values is not None else None)
 

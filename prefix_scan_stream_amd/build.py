@@ -77,9 +77,32 @@ def build(verbose: bool = False, lib: str = LIB, build_dir: str = BUILD, defines
     return lib
 
 
+CEILING_LIB = os.path.join(PKG, "libls_ceiling.so")
+CEILING_HEADER = os.path.join(ROOT, "include", "ls_ceiling.h")
+
+
+def build_ceiling_lib(verbose: bool = False) -> str:
+    """libls_ceiling.so: the read / write / copy ceiling kernels the benchmark times
+    beside the library (include/ls_ceiling.h); not part of libscan."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile("ls_ceiling.hip")
+    with open(CEILING_HEADER) as f:
+        names = sorted(set(re.findall(r"^int\s+(ls_ceiling_[a-z]+)\s*\(", f.read(), re.M)))
+    vs = os.path.join(BUILD, "ceiling_exports.map")
+    with open(vs, "w") as f:
+        f.write("{\n  global:\n" + "".join(f"    {n};\n" for n in names) + "  local: *;\n};\n")
+    tmp = CEILING_LIB + f".tmp{os.getpid()}"
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj,
+                           f"-Wl,--version-script={vs}"])
+    os.replace(tmp, CEILING_LIB)
+    if verbose:
+        print(f"built {CEILING_LIB}")
+    return CEILING_LIB
+
+
 def build_bounded_wait_test_lib(verbose: bool = False) -> str:
     """libscan_spin1.so: bounded waits give up after one empty poll (test use only)."""
-    return build(verbose, SPIN1_LIB, os.path.join(BUILD, "spin1"), ("-DLS_LOOKBACK_SPIN_LIMIT=1",))
+    return build(verbose, SPIN1_LIB, os.path.join(BUILD, "spin1"), ("-DLS_WAIT_LIMIT_TICKS=0",))
 
 
 if __name__ == "__main__":

@@ -36,8 +36,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
-// n elements of 4 bytes must be addressable without wrapping
-bool size_ok(int64_t n) { return n >= 0 && n <= (INT64_MAX / 8); }
+// Element counts the kernels can index: tile ids are 32 bits, compaction counts
+// 36 bits.
+bool size_ok(int64_t n) { return n >= 0 && n <= LS_MAX_N; }
+bool compact_size_ok(int64_t n) { return n >= 0 && n <= LS_COMPACT_MAX_N; }
 
 ls_status from_hip(hipError_t e) { return e == hipSuccess ? LS_OK : LS_ERR_HIP; }
 
@@ -95,7 +97,7 @@ ls_status compact_common(const void* in, const uint8_t* flags, void* out, int64_
 {
     const bool has_in = src == 0 || pay == 0;
     const bool has_flags = src == 1;
-    if (!size_ok(n) || !valid_dtype(t) || !valid_cmp(cmp) || count == nullptr || !aligned(count, 8))
+    if (!compact_size_ok(n) || !valid_dtype(t) || !valid_cmp(cmp) || count == nullptr || !aligned(count, 8))
         return LS_ERR_INVALID_ARG;
     if (pay == 1 && n > int64_t(UINT32_MAX))
         return LS_ERR_INVALID_ARG;
@@ -190,8 +192,33 @@ const char* ls_status_string(ls_status s)
     case LS_ERR_UNSUPPORTED: return "LS_ERR_UNSUPPORTED: operator not defined for this element type";
     case LS_ERR_WORKSPACE: return "LS_ERR_WORKSPACE: workspace missing or too small";
     case LS_ERR_HIP: return "LS_ERR_HIP: the HIP runtime reported an error";
+    case LS_ERR_INCOMPLETE:
+        return "LS_ERR_INCOMPLETE: a call on this workspace gave up waiting for another tile; its output is "
+               "incomplete (re-initialise the workspace)";
     }
     return "unknown libscan status";
+}
+
+ls_status ls_workspace_init(void* ws, size_t ws_bytes, void* stream)
+{
+    if (ws == nullptr || ws_bytes < 256 || ws_bytes % 16 != 0 || !aligned(ws, 16))
+        return LS_ERR_INVALID_ARG;
+    return from_hip(ls::init_workspace(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ls_status ls_workspace_check(const void* ws, uint32_t* flags, void* stream)
+{
+    if (ws == nullptr || !aligned(ws, 16))
+        return LS_ERR_INVALID_ARG;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    const char* p = reinterpret_cast<const char*>(ws) + 8;  // the header's error word
+    if (hipMemcpyAsync(&word, p, sizeof word, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return LS_ERR_HIP;
+    if (flags != nullptr)
+        *flags = word;
+    return word == 0 ? LS_OK : LS_ERR_INCOMPLETE;
 }
 
 ls_status ls_scan_workspace_bytes(int64_t n, ls_dtype t, ls_op op, size_t* bytes)
@@ -241,7 +268,7 @@ ls_status scan_noalloc(const void* in, void* out, int64_t n, ls_dtype t, ls_op o
 
 ls_status ls_compact_workspace_bytes(int64_t n, ls_dtype t, size_t* bytes)
 {
-    if (bytes == nullptr || !size_ok(n) || !valid_dtype(t))
+    if (bytes == nullptr || !compact_size_ok(n) || !valid_dtype(t))
         return LS_ERR_INVALID_ARG;
     *bytes = ls::compact_workspace_bytes(n);
     return LS_OK;

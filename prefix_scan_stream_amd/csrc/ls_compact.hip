@@ -115,6 +115,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
     __shared__ uint32_t s_arrive;          // data waves done counting (all tiles so far)
     __shared__ int64_t s_next[2];          // id of tile k+1, by step parity
     __shared__ int64_t s_base;
+    __shared__ uint32_t s_ep;              // the call's epoch (the same in every ticket of the call)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -229,30 +230,67 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
             }
             if (lane == 0) {
                 s_kept[buf] = kept;
-                status_store(status_word(status, t), CountCodec::pack(t == 0 ? ST_PREFIX : ST_AGGREGATE, kept));
+                status_store(status_word(status, t),
+                             CountCodec::pack(t == 0 ? ST_PREFIX : ST_AGGREGATE, kept, s_ep));
             }
         }
     };
 
-    // prologue: tile 0 of the block, counted; the id of tile 1
+    // Recount of full tile j by the control wave: the fallback of a look-back that
+    // runs out of time (the tile's block may not have been dispatched yet).  A count
+    // of kept elements does not depend on the order in which it is summed.
+    auto recount = [&](int64_t j) -> uint64_t {
+        const int64_t tb = j * CP_TILE;
+        uint32_t c = 0;
+        for (uint32_t q = uint32_t(lane); q < uint32_t(CP_TILE / 4); q += 64) {  // elements 4q .. 4q+3
+            if constexpr (SRC == SRC_FLAGS) {
+                const __amdgpu_buffer_rsrc_t rfl = make_rsrc(flags + tb, uint32_t(CP_TILE));
+                uint32_t w = 0;
+                if (FLAG4) {
+                    w = __builtin_amdgcn_raw_buffer_load_b32(rfl, 4u * q, 0, CACHE_NT);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        w |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(rfl, 4u * q + b, 0, CACHE_NT)) << (8 * b);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    c += ((w >> (8 * b)) & 0xffu) != 0u;
+            } else {
+                const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + tb, uint32_t(CP_TILE) * 4u);
+                const Run4<uint32_t> v = VEC ? load_run_x4<uint32_t>(rin, 16u * q, 0) : load_run_x1<uint32_t>(rin, 16u * q, 0);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    c += pred_bit<DT>(v.v[b], thr, table);
+            }
+        }
+        return uint64_t(read_lane(wave_inclusive_scan<SumU32>(c), 63));
+    };
+
+    // prologue: the block's first tile (its block index), counted.  Tiles go to
+    // blocks by index: block b handles b, b + G, b + 2G, ... for G blocks.
     if (tid == 0) {
         s_arrive = 0;
-        s_next[1] = take_tile_id(hdr);
+        s_next[1] = blockIdx.x;
+        s_ep = read_epoch(hdr);
     }
     __syncthreads();
+    const uint32_t ep = s_ep;
     int64_t cur = s_next[1];
-    if (cur >= num_tiles)
-        return;  // uniform over the block
-    if (!ctrl) {
-        uint32_t g = 0;
+    if (cur >= num_tiles) {  // never with the launch's grid; uniform over the block
         if (tid == 0)
-            g = take_tile_id(hdr);
+            mark_started(hdr);
+        return;
+    }
+    if (!ctrl) {
 #pragma unroll
         for (int j = 0; j < CP_CHUNKS; ++j)
             load_run(cur, j);
         count_tile(cur, 0);
-        if (tid == 0)
-            s_next[0] = g;
+        if (tid == 0) {
+            s_next[0] = cur + gridDim.x;
+            mark_started(hdr);  // the epoch read completed before the barrier above (its LDS copy)
+        }
     }
     __syncthreads();
 
@@ -281,9 +319,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
                 }
             };
             if (next < num_tiles) {
-                uint32_t g = 0;
-                if (tid == 0)
-                    g = take_tile_id(hdr);  // id of tile k+2, used a step from now
+                const int64_t g = next + gridDim.x;  // the block's tile after next
 #pragma unroll
                 for (int j = 0; j < CP_CHUNKS; ++j) {
                     stage_run(j);
@@ -300,14 +336,16 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
         } else {
             int64_t base = 0;
             if (cur != 0) {
-                base = int64_t(lookback<CountCodec, CP_LB_WIDE>(status, cur, hdr));
+                base = int64_t(lookback<CountCodec, CP_LB_WIDE>(status, cur, ep, hdr, recount));
                 if (lane == 0)
-                    status_store(status_word(status, cur), CountCodec::pack(ST_PREFIX, uint64_t(base) + kept));
+                    status_store(status_word(status, cur), CountCodec::pack(ST_PREFIX, uint64_t(base) + kept, ep));
             }
             if (lane == 0) {
                 s_base = base;
-                if (cur == num_tiles - 1)
+                if (cur == num_tiles - 1) {
                     *count = base + int64_t(kept);
+                    end_call(hdr, ep, gridDim.x);
+                }
             }
         }
         __syncthreads();  // tile k staged, its offset known, tile k+1 counted
@@ -440,9 +478,7 @@ hipError_t launch_compact_general(const void* in, const uint8_t* flags, void* ou
         return hipGetLastError();
     }
     const int64_t tiles = cp_tiles(n);
-    hipError_t e = clear_workspace(ws, tiles, s);
-    if (e != hipSuccess)
-        return e;
+    hipError_t e = hipSuccess;
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
     const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;

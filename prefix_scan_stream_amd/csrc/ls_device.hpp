@@ -333,8 +333,12 @@ __device__ __forceinline__ void store_run(T* __restrict__ p, int64_t idx, int64_
 // One 64-bit word per tile, published and read with agent-scope atomics, so the
 // flag and the value travel together and no other memory needs ordering.  Agent
 // scope makes the accesses coherent across the eight XCDs (their L2s are not).
-//   32-bit payload (scans): bits 63..32 = flag, bits 31..0 = value bits.
-//   62-bit payload (compaction counts): bits 63..62 = flag, bits 61..0 = count.
+// Every word also carries the epoch of the call that wrote it (below); a word
+// whose epoch is not the reader's reads as empty, so words left by earlier calls
+// never need clearing.
+//   32-bit payload (scans): bits 63..62 flag, 61..32 epoch (30 bits), 31..0 value.
+//   36-bit payload (compaction counts): 63..62 flag, 61..36 epoch (26 bits),
+//     35..0 count.
 // Each tile's word sits alone in a 256-byte slot.  Packed eight to a cache line,
 // the words of neighbouring tiles are published and polled by hundreds of waves
 // at once through one line; measured on MI355X that contention slowed the whole
@@ -357,28 +361,112 @@ __device__ __forceinline__ uint64_t status_load(const uint64_t* p)
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded waiting: a look-back gives up after this many empty polls and records
-// the fact in the workspace error word, so a defect can never hang the GPU.  In
-// a correct run the wait is a few microseconds; the cap is far above that.
-#ifndef LS_LOOKBACK_SPIN_LIMIT
-#define LS_LOOKBACK_SPIN_LIMIT (1 << 16)
+// Bounded waiting: a wait that sees no progress for about one second (the
+// wall clock runs at 100 MHz on MI355X) gives up and records the fact in the
+// workspace error word, so a defect can never hang the GPU.  In a correct run a
+// wait lasts microseconds.  A test build sets the limit to 0: every wait then
+// gives up after its first empty poll.
+#ifndef LS_WAIT_LIMIT_TICKS
+#define LS_WAIT_LIMIT_TICKS 100000000ull
 #endif
-constexpr int LOOKBACK_SPIN_LIMIT = LS_LOOKBACK_SPIN_LIMIT;  // a test build sets 1 to force the give-up
-constexpr uint32_t WS_ERR_LOOKBACK_TIMEOUT = 1u;
+constexpr uint64_t WAIT_LIMIT_TICKS = LS_WAIT_LIMIT_TICKS;
+constexpr uint32_t WS_ERR_WAIT_TIMEOUT = 1u;  // a wait gave up: that call's output is incomplete
+constexpr uint32_t WS_ERR_BAD_TICKET = 2u;    // a tile id past the call's tiles (workspace not initialised,
+                                              // or shared by calls that overlap)
 
-// Workspace header (first 256 bytes of every workspace).
+// Start of a wait, and whether its time is up (read only after an empty poll).
+__device__ __forceinline__ uint64_t wait_start() { return wall_clock64(); }
+__device__ __forceinline__ bool wait_expired(uint64_t start) { return wall_clock64() - start >= WAIT_LIMIT_TICKS; }
+
+// Workspace header (first 256 bytes of every workspace).  A workspace starts
+// zero-filled (ls_workspace_init) and every call leaves it ready for the next:
+// the epoch advanced, the counters back at 0.  Calls need no clearing launch.
 struct WsHeader {
-    uint32_t tile_counter;  // dynamic tile ids: the order in which blocks start
-    uint32_t error_flags;   // WS_ERR_* bits of the last call
-    uint32_t pad[62];
+    uint64_t ticket;       // bits 63..32: the current call's epoch; bits 31..0: tickets handed out so far
+    uint32_t error_flags;  // WS_ERR_* bits, kept until the workspace is initialised again
+    uint32_t started;      // block-index kernels: blocks that have read the current epoch
+    uint32_t pad[60];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
 
-// Tile id in start order: a block only ever waits for tiles that were handed to
-// blocks which started before it, so every wait is for a running block.
-__device__ __forceinline__ uint32_t take_tile_id(WsHeader* h)
+__device__ __forceinline__ uint32_t ticket_tile(uint64_t t) { return uint32_t(t); }
+__device__ __forceinline__ uint32_t ticket_epoch(uint64_t t) { return uint32_t(t >> 32); }
+
+// The next call on this workspace runs under the next epoch, with no tickets out.
+__device__ __forceinline__ void start_next_epoch(WsHeader* h, uint32_t epoch)
 {
-    return __hip_atomic_fetch_add(&h->tile_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&h->ticket, uint64_t(epoch + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Two ways of giving tiles to blocks.
+//
+// Tickets (segmented scans, the fixed-order and the affine-map scans): a block
+// takes the next tile id from a counter in the order blocks start, so a block only
+// ever waits for tiles that were handed to blocks which started before it: every
+// wait is for a running block.  The ticket carries the call's epoch in its high
+// half; the block that takes the call's last tile (all tickets are then out)
+// starts the next epoch.
+__device__ __forceinline__ uint64_t take_ticket(WsHeader* h)
+{
+    return __hip_atomic_fetch_add(&h->ticket, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block index (the plain single-pass scan and the compaction): tile = the block's
+// index, which costs no atomic at the start of a block (one device-scope atomic on
+// one address serializes at about 12 ns on MI355X, which is most of the gap
+// between a tiled copy and the scan).  Without tickets, a tile may wait for a tile
+// whose block has not been dispatched, so every such wait has a fallback that
+// needs no other block: after a time limit the waiting tile computes what it
+// waits for from the input itself (ls_device.hpp: replay_prefix, and the
+// recounting look-back of the compaction).  The call's epoch is read from the
+// header by each block's thread 0, which then counts the block as started; the
+// block that finishes the call's last tile waits until every block has started
+// (so none can read the epoch afterwards) and then starts the next epoch.
+__device__ __forceinline__ uint32_t read_epoch(WsHeader* h)
+{
+    return ticket_epoch(__hip_atomic_load(&h->ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Once per block, by the thread that read the epoch, after it has stored
+// something computed from the epoch: that store waits for the read, so the read
+// is complete before this count is issued.  The count itself is relaxed: a
+// release here would write back the L2 of the XCD for every block (measured: the
+// scan of 2^28 at 831 instead of 325 us).  Nothing waits for its result.
+__device__ __forceinline__ void mark_started(WsHeader* h)
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keeps the compiler from issuing it earlier
+    __hip_atomic_fetch_add(&h->started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A wait that always ends in a correct run (the blocks it waits for start as soon
+// as others finish); its limit only guards against defects.
+constexpr uint64_t END_CALL_LIMIT_TICKS = 100000000ull;
+
+// The chased scan needs no count of started blocks: if the call's last tile
+// obtained its prefix from the chasing wave, that wave had seen the totals of
+// all earlier tiles, each written by its own block after reading the epoch, so
+// every block has started.  Only a last tile that replayed its prefix must first
+// see every earlier total word published (await_totals) before starting the next
+// epoch.  Called by one whole wave.
+
+__device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits);
+
+// By one thread of the block that finished the call's last tile, after its own
+// mark_started.  In the usual case every block started long before, because the
+// last tile's prefix needed every other tile's total.
+__device__ __forceinline__ void end_call(WsHeader* h, uint32_t epoch, uint32_t blocks)
+{
+    const uint64_t t0 = wall_clock64();
+    // relaxed: the epoch store below depends on this loop's exit, so it is issued
+    // only after the count was seen complete
+    while (__hip_atomic_load(&h->started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < blocks) {
+        if (uint64_t(wall_clock64()) - t0 >= END_CALL_LIMIT_TICKS) {
+            flag_error(h, WS_ERR_WAIT_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __hip_atomic_store(&h->started, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    start_next_epoch(h, epoch);
 }
 
 __device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits)
@@ -390,15 +478,19 @@ __device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits)
 // Status codecs: how a 64-bit status word holds (flag, value) and how values of
 // a window are combined across a wave.
 //
-// Scan values: the operator's 32-bit element, flag in the high half.
+// Scan values: the operator's 32-bit element in the low half.
 template <class Op>
 struct ScanCodec {
     using V = typename Op::T;
-    static __device__ __forceinline__ uint32_t flag(uint64_t w) { return uint32_t(w >> 32); }
-    static __device__ __forceinline__ V value(uint64_t w) { return from_bits<V>(uint32_t(w)); }
-    static __device__ __forceinline__ uint64_t pack(uint32_t f, V v)
+    static constexpr uint32_t EPOCH_MASK = (1u << 30) - 1u;
+    static __device__ __forceinline__ uint32_t flag(uint64_t w, uint32_t ep)
     {
-        return (uint64_t(f) << 32) | uint64_t(to_bits(v));
+        return ((uint32_t(w >> 32) & EPOCH_MASK) == (ep & EPOCH_MASK)) ? uint32_t(w >> 62) : ST_EMPTY;
+    }
+    static __device__ __forceinline__ V value(uint64_t w) { return from_bits<V>(uint32_t(w)); }
+    static __device__ __forceinline__ uint64_t pack(uint32_t f, V v, uint32_t ep)
+    {
+        return (uint64_t(f) << 62) | (uint64_t(ep & EPOCH_MASK) << 32) | uint64_t(to_bits(v));
     }
     static __device__ __forceinline__ V identity() { return Op::identity(); }
     static __device__ __forceinline__ V apply(V a, V b) { return Op::apply(a, b); }
@@ -411,26 +503,41 @@ struct ScanCodec {
     }
 };
 
-// Compaction counts: 62-bit count, flag in the top two bits.  A lane's partial
-// is small (a few tile counts) except on lane `hi`, whose partial includes a
-// full prefix; the small ones are summed in 32 bits, the big one read whole.
+// Compaction counts: a 36-bit count (n < 2^36 elements).  Tile totals are at
+// most one tile's elements; only full prefixes are large.
 struct CountCodec {
     using V = uint64_t;
-    static constexpr uint64_t MASK = (uint64_t(1) << 62) - 1;
-    static __device__ __forceinline__ uint32_t flag(uint64_t w) { return uint32_t(w >> 62); }
+    static constexpr uint64_t MASK = (uint64_t(1) << 36) - 1;
+    static constexpr uint32_t EPOCH_MASK = (1u << 26) - 1u;
+    static __device__ __forceinline__ uint32_t flag(uint64_t w, uint32_t ep)
+    {
+        return ((uint32_t(w >> 36) & EPOCH_MASK) == (ep & EPOCH_MASK)) ? uint32_t(w >> 62) : ST_EMPTY;
+    }
     static __device__ __forceinline__ V value(uint64_t w) { return w & MASK; }
-    static __device__ __forceinline__ uint64_t pack(uint32_t f, V v) { return (uint64_t(f) << 62) | (v & MASK); }
+    static __device__ __forceinline__ uint64_t pack(uint32_t f, V v, uint32_t ep)
+    {
+        return (uint64_t(f) << 62) | (uint64_t(ep & EPOCH_MASK) << 36) | (v & MASK);
+    }
     static __device__ __forceinline__ V identity() { return 0; }
     static __device__ __forceinline__ V apply(V a, V b) { return a + b; }
+    // The chasing wave scans tile totals (each at most one tile, so 64 of them
+    // fit in 32 bits) and adds the 64-bit base afterwards.
+    static __device__ __forceinline__ V wave_scan(V v) { return wave_inclusive_scan<SumU32>(uint32_t(v)); }
+    static __device__ __forceinline__ V lane(V v, int l)
+    {
+        const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), l);
+        const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(v >> 32), l);
+        return (uint64_t(hi) << 32) | lo;
+    }
+    // A lane's partial is small (a few tile counts) except on lane `hi`, whose
+    // partial includes a full prefix; the small ones are summed in 32 bits, the
+    // big one read whole.
     static __device__ __forceinline__ V wave_reduce(V part, int hi)
     {
         const uint32_t small = (lane_id() > hi) ? uint32_t(part) : 0u;
         V r = read_lane(wave_inclusive_scan<SumU32>(small), 63);
-        if (hi >= 0) {
-            const uint32_t lo32 = __builtin_amdgcn_readlane(uint32_t(part), hi);
-            const uint32_t hi32 = __builtin_amdgcn_readlane(uint32_t(part >> 32), hi);
-            r += (uint64_t(hi32) << 32) | lo32;
-        }
+        if (hi >= 0)
+            r += lane(part, hi);
         return r;
     }
 };
@@ -455,63 +562,86 @@ constexpr int LB_WINDOW = 64;
 constexpr int LB_NEAR = 8;      // tiles read by the first, narrow poll
 constexpr int LB_SLEEP = 32;    // s_sleep units (64 clocks each) between polls
 
-template <class Codec, int WIDE = LB_WINDOW>
-__device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHeader* hdr)
+// No fallback: a look-back that runs out of time gives up (tickets guarantee that
+// this only happens on a defect) and reports it in the error word.
+struct NoRecount {
+};
+
+// With a recount function (block-index tiles), a look-back that runs out of time
+// computes the totals of the window's unpublished tiles itself (recount(j), called
+// by the whole wave, must return tile j's exact total) and goes on.
+template <class Codec, int WIDE = LB_WINDOW, class Recount = NoRecount>
+__device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, uint32_t ep, WsHeader* hdr,
+                                      Recount recount = Recount())
 {
     static_assert(WIDE >= LB_NEAR && WIDE <= LB_WINDOW, "a wide poll reads LB_NEAR to 64 tiles");
     using V = typename Codec::V;
     const int lane = lane_id();
     auto word = [&](int64_t idx) -> uint64_t {
-        return idx >= 0 ? status_load(status + idx * STATUS_STRIDE) : Codec::pack(ST_PREFIX, Codec::identity());
+        return idx >= 0 ? status_load(status + idx * STATUS_STRIDE) : Codec::pack(ST_PREFIX, Codec::identity(), ep);
     };
     if constexpr (WIDE > LB_NEAR) {
         // narrow first poll: lanes 56..63 read the eight nearest tiles; the
         // other lanes stand for tiles that do not take part (identity totals).
         // With WIDE == LB_NEAR the loop's first poll reads the same words.
         const bool near = lane >= LB_WINDOW - LB_NEAR;
-        const uint64_t w = near ? word(tile - LB_WINDOW + lane) : Codec::pack(ST_AGGREGATE, Codec::identity());
-        const uint64_t has = __ballot(near && Codec::flag(w) == ST_PREFIX);
+        const uint64_t w = near ? word(tile - LB_WINDOW + lane) : Codec::pack(ST_AGGREGATE, Codec::identity(), ep);
+        const uint64_t has = __ballot(near && Codec::flag(w, ep) == ST_PREFIX);
         const int hi = has ? 63 - __builtin_clzll(has) : -1;
-        if (hi >= 0 && !__ballot(lane > hi && Codec::flag(w) == ST_EMPTY))
+        if (hi >= 0 && !__ballot(lane > hi && Codec::flag(w, ep) == ST_EMPTY))
             return Codec::wave_reduce(lane >= hi ? Codec::value(w) : Codec::identity(), hi);
     }
     V excl = Codec::identity();
     int64_t last = tile - 1;
-    int spins = 0;
+    uint64_t t0 = wait_start();
     for (;;) {
         // lanes 64 - WIDE .. 63 read the WIDE newest tiles not yet combined
         const bool act = lane >= LB_WINDOW - WIDE;
-        const uint64_t w = act ? word(last - (LB_WINDOW - 1) + lane) : Codec::pack(ST_AGGREGATE, Codec::identity());
-        const uint64_t has = __ballot(act && Codec::flag(w) == ST_PREFIX);
+        uint64_t w = act ? word(last - (LB_WINDOW - 1) + lane) : Codec::pack(ST_AGGREGATE, Codec::identity(), ep);
+        const uint64_t has = __ballot(act && Codec::flag(w, ep) == ST_PREFIX);
         const int hi = has ? 63 - __builtin_clzll(has) : -1;
-        if (__ballot(act && lane > hi && Codec::flag(w) == ST_EMPTY)) {
-            if (++spins < LOOKBACK_SPIN_LIMIT) {
+        uint64_t empty = __ballot(act && lane > hi && Codec::flag(w, ep) == ST_EMPTY);
+        if (empty) {
+            if (!wait_expired(t0)) {
                 __builtin_amdgcn_s_sleep(LB_SLEEP);
                 continue;
             }
-            if (lane == 0)
-                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
-            return excl;  // only reached on a defect; the error word reports it
+            if constexpr (__is_same(Recount, NoRecount)) {
+                if (lane == 0)
+                    flag_error(hdr, WS_ERR_WAIT_TIMEOUT);
+                return excl;  // only reached on a defect; the error word reports it
+            } else {
+                while (empty) {  // the fallback: count the missing tiles here
+                    const int m = __builtin_ctzll(empty);
+                    empty &= empty - 1;
+                    const typename Codec::V v = recount(last - (LB_WINDOW - 1) + m);
+                    if (lane == m)
+                        w = Codec::pack(ST_AGGREGATE, v, ep);
+                }
+            }
         }
         const V part = lane >= hi ? Codec::value(w) : Codec::identity();
         excl = Codec::apply(Codec::wave_reduce(part, hi), excl);  // older tiles on the left
         if (hi >= 0)
             return excl;
         last -= WIDE;
+        t0 = wait_start();  // progress: the next window's wait starts afresh
     }
 }
 
 // ---------------------------------------------------------------- chased prefixes
 // The single-pass scan does not let every tile walk back on its own.  One wave
 // (the one that scanned tile 0) stays resident after its tile and moves the
-// "full prefix" frontier forward for everyone: it polls the status words of the
+// "full prefix" frontier forward for everyone: it polls the total words of the
 // current group of 64 tiles, takes the run of consecutive tiles that have
 // published their totals, scans them across the wave, and publishes a full prefix
 // for each (chase_prefixes below).  Every other tile publishes its total and then
-// polls one word, its predecessor's, until that word holds a full prefix: its
-// own exclusive prefix.  Only the chasing wave writes full prefixes (besides
-// tile 0), so each tile's prefix is computed once and every tile sees the same
-// value.
+// polls one word, its predecessor's prefix word, until it holds the full prefix:
+// its own exclusive prefix.  A tile slot holds two words: the prefix word (word
+// 0, written only with full prefixes) and the total word (word TOTAL_WORD, the
+// tile's own total, never overwritten).  Every writer of a word writes the same
+// value, so the order of writes does not matter.  (Side by side in one cache line
+// they measured 1 us faster on the 2^28 scan than on separate lines.)
 //
 // Why: traced on MI355X (int32 scan of 2^28), walking tiles took 5.7 polls of
 // 8 words each (about 45 status reads) to reach a published prefix, because the
@@ -525,35 +655,41 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, WsHe
 // slower as well (358 / 390 us).
 //
 // Progress: the chaser only reads totals, and a tile publishes its total without
-// waiting for anything; a tile with an id is resident, because ids are taken in
-// start order.  So the frontier always reaches every tile, and both loops are
-// bounded like the look-back (the error word reports a cap that is hit).
+// waiting for anything.  With tickets, a tile with an id is resident, so the
+// frontier always reaches every tile; with block-index tiles a waiting tile that
+// runs out of time replays the chaser's arithmetic itself (replay_prefix).
+constexpr int TOTAL_WORD = 1;       // the total word's offset in a tile slot (64-bit words)
 constexpr int LB_WAIT_SLEEP = 8;    // s_sleep units between a tile's polls of its predecessor
 constexpr int LB_CHASE_SLEEP = 2;   // between chaser polls that found nothing new
+constexpr int CHASE_GROUP = 64;     // tiles per group of the chaser's scans (one per lane)
 
-// Exclusive prefix of `tile` (>= 1): the full prefix that the chaser publishes
-// in the status word of tile - 1.  Called by a whole wave; every lane reads the
-// same word.
+__device__ __forceinline__ uint64_t* total_word(uint64_t* status, int64_t tile)
+{
+    return status + tile * STATUS_STRIDE + TOTAL_WORD;
+}
+
+// Waits for the full prefix of tile - 1 (tile >= 1): the exclusive prefix of
+// `tile`.  Called by a whole wave; every lane reads the same word.  Returns false
+// when the time limit passes first (`out` is then untouched).
 template <class Codec>
-__device__ typename Codec::V wait_prefix(const uint64_t* status, int64_t tile, WsHeader* hdr)
+__device__ bool wait_prefix(const uint64_t* status, int64_t tile, uint32_t ep, typename Codec::V& out)
 {
     const uint64_t* p = status + (tile - 1) * STATUS_STRIDE;
-    int spins = 0;
+    const uint64_t t0 = wait_start();
     for (;;) {
         const uint64_t w = status_load(p);
-        if (__ballot(Codec::flag(w) == ST_PREFIX))
-            return Codec::value(w);
-        if (++spins >= LOOKBACK_SPIN_LIMIT) {
-            if (lane_id() == 0)
-                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
-            return Codec::identity();  // only reached on a defect; the error word reports it
+        if (__ballot(Codec::flag(w, ep) == ST_PREFIX)) {
+            out = Codec::value(w);
+            return true;
         }
+        if (wait_expired(t0))
+            return false;
         __builtin_amdgcn_s_sleep(LB_WAIT_SLEEP);
     }
 }
 
 // Publishes the full prefix of tiles 1 .. num_tiles - 1, in order, given the
-// full prefix of tile 0.  Called by one whole wave, after tile 0 is published.
+// total of tile 0.  Called by one whole wave, after tile 0 is published.
 // Tiles form groups of 64 aligned to tile 0, lane l standing for tile 64 G + l.
 // The wave keeps the totals of the group's tiles it has seen in its lanes and
 // polls only the lanes still missing; once lanes 0 .. k-1 hold totals it scans the
@@ -564,48 +700,122 @@ __device__ typename Codec::V wait_prefix(const uint64_t* status, int64_t tile, W
 // every run (MI355X, float32 sum of 2^26: one distinct result in 10 runs, against
 // 10 in 10 for windows that start at the frontier, at the same speed).  A tile
 // whose full prefix does not depend on earlier tiles (a segmented tile containing a
-// head) may publish it itself; the wave takes such a word as that tile's total --
-// its scan gives the same value there -- and does not publish it again.
+// head) may publish it itself: the wave's scan gives the same value there.
+// A wait without progress past the time limit ends the wave silently: waiting
+// tiles then run out of time themselves and either replay (block-index tiles) or
+// report it (tickets).
 template <class Codec>
-__device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V prefix, WsHeader* hdr)
+__device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V total0, uint32_t ep)
 {
     using V = typename Codec::V;
     const int lane = lane_id();
     int64_t g0 = 0;                                  // first tile of the current group
     V base = Codec::identity();                      // full prefix of tile g0 - 1
-    V tot = lane == 0 ? prefix : Codec::identity();  // totals of the group's tiles seen so far
+    V tot = lane == 0 ? total0 : Codec::identity();  // totals of the group's tiles seen so far
     int have = 1;                                    // lanes 0 .. have-1 hold their totals
-    int idle = 0;
+    uint64_t t0 = wait_start();
     while (g0 + have < num_tiles) {
         const int64_t idx = g0 + lane;
         const bool want = lane >= have && idx < num_tiles;
-        const uint64_t w = want ? status_load(status + idx * STATUS_STRIDE) : 0ull;
-        const bool pub = want && Codec::flag(w) == ST_AGGREGATE;  // still to be published
-        const bool ready = lane < have || pub || (want && Codec::flag(w) == ST_PREFIX);
+        const uint64_t w = want ? status_load(total_word(status, idx)) : 0ull;
+        const bool ready = lane < have || (want && Codec::flag(w, ep) == ST_AGGREGATE);
         const uint64_t miss = __ballot(!ready);
         const int k = miss ? __builtin_ctzll(miss) : 64;  // lanes 0 .. k-1 now hold totals
         if (k == have) {
-            if (++idle >= LOOKBACK_SPIN_LIMIT) {
-                if (lane == 0)
-                    flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
-                return;  // only reached on a defect; the error word reports it
-            }
+            if (wait_expired(t0))
+                return;
             __builtin_amdgcn_s_sleep(LB_CHASE_SLEEP);
             continue;
         }
-        idle = 0;
+        t0 = wait_start();
         if (lane >= have && lane < k)
             tot = Codec::value(w);
         // older on the left: base (+) totals of tiles g0 .. g0 + lane
         const V inc = Codec::apply(base, Codec::wave_scan(lane < k ? tot : Codec::identity()));
-        if (lane >= have && lane < k && pub)
-            status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc));
+        if (lane >= have && lane < k)
+            status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc, ep));
         have = k;
         if (have == 64) {
             base = Codec::lane(inc, 63);
             g0 += 64;
             have = 0;
             tot = Codec::identity();
+        }
+    }
+}
+
+// The full prefix of tile `last` exactly as chase_prefixes computes it, by one
+// wave that depends on no other block: the fallback of a block-index tile whose
+// wait ran out of time.  Group bases come from published prefix words where they
+// exist (a group's base is the full prefix of the tile before it); tile totals
+// from total words, or, for a tile that has not published one, from
+// total_of(j), which must compute the total exactly as tile j's own block does
+// (the same operations in the same order, so float results match bit for bit).
+// The full prefixes it computes (each group end it passes, and `last`) are
+// published on the way: the same values the chasing wave writes.  Totals are not:
+// a total word is only ever written by its tile's own block, so a published total
+// also says that block has started (read the call's epoch).
+template <class Codec, class TotalFn>
+__device__ typename Codec::V replay_prefix(uint64_t* status, int64_t last, uint32_t ep, TotalFn total_of)
+{
+    using V = typename Codec::V;
+    const int lane = lane_id();
+    const int64_t g = last / CHASE_GROUP;
+    // the latest group at or before g whose base is published (group 0's is the identity)
+    int64_t gb = g;
+    V base = Codec::identity();
+    for (; gb > 0; --gb) {
+        const uint64_t w = status_load(status + (gb * CHASE_GROUP - 1) * STATUS_STRIDE);
+        if (Codec::flag(w, ep) == ST_PREFIX) {
+            base = Codec::value(w);
+            break;
+        }
+    }
+    for (int64_t gg = gb;; ++gg) {
+        const int64_t first = gg * CHASE_GROUP;
+        const int64_t idx = first + lane;
+        const bool want = idx <= last;
+        const uint64_t w = want ? status_load(total_word(status, idx)) : 0ull;
+        V tot = want && Codec::flag(w, ep) == ST_AGGREGATE ? Codec::value(w) : Codec::identity();
+        uint64_t missing = __ballot(want && Codec::flag(w, ep) != ST_AGGREGATE);
+        while (missing) {
+            const int m = __builtin_ctzll(missing);
+            missing &= missing - 1;
+            const V v = total_of(first + m);  // the whole wave computes it
+            if (lane == m)
+                tot = v;
+        }
+        const V inc = Codec::apply(base, Codec::wave_scan(tot));
+        if (gg == g) {
+            const int l = int(last - first);
+            if (lane == l)
+                status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc, ep));
+            return Codec::lane(inc, l);
+        }
+        base = Codec::lane(inc, CHASE_GROUP - 1);
+        if (lane == CHASE_GROUP - 1)
+            status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc, ep));
+    }
+}
+
+// Waits until tiles 0 .. last-1 have each published their own total under epoch
+// `ep` (see end of call above).  One whole wave; bounded like end_call.
+template <class Codec>
+__device__ void await_totals(uint64_t* status, int64_t last, uint32_t ep, WsHeader* hdr)
+{
+    const uint64_t t0 = wall_clock64();
+    for (int64_t first = 0; first < last; first += 64) {
+        const int64_t idx = first + lane_id();
+        for (;;) {
+            const bool ok = idx >= last || Codec::flag(status_load(total_word(status, idx)), ep) == ST_AGGREGATE;
+            if (!__ballot(!ok))
+                break;
+            if (uint64_t(wall_clock64()) - t0 >= END_CALL_LIMIT_TICKS) {
+                if (lane_id() == 0)
+                    flag_error(hdr, WS_ERR_WAIT_TIMEOUT);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(8);
         }
     }
 }
@@ -622,24 +832,24 @@ __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Cod
 constexpr int LB_GROUP = 64;
 
 template <class Codec>
-__device__ typename Codec::V lookback_grouped(const uint64_t* status, int64_t tile, WsHeader* hdr)
+__device__ typename Codec::V lookback_grouped(const uint64_t* status, int64_t tile, uint32_t ep, WsHeader* hdr)
 {
     const int lane = lane_id();
     const int64_t g0 = tile - tile % LB_GROUP;  // first tile of this tile's group
     const int before = int(tile - g0);         // tiles of the group before this one
     const bool needed = lane == 0 ? g0 > 0 : lane <= before;
     const int64_t idx = lane == 0 ? g0 - 1 : g0 + lane - 1;
-    int spins = 0;
+    const uint64_t t0 = wait_start();
     for (;;) {
         const uint64_t w = needed ? status_load(status + idx * STATUS_STRIDE)
-                                  : Codec::pack(ST_AGGREGATE, Codec::identity());
-        const uint32_t f = Codec::flag(w);
+                                  : Codec::pack(ST_AGGREGATE, Codec::identity(), ep);
+        const uint32_t f = Codec::flag(w, ep);
         const bool ready = !needed || (lane == 0 ? f == ST_PREFIX : f != ST_EMPTY);
         if (!__ballot(!ready))
             return Codec::wave_reduce(needed ? Codec::value(w) : Codec::identity(), -1);
-        if (++spins >= LOOKBACK_SPIN_LIMIT) {
+        if (wait_expired(t0)) {
             if (lane == 0)
-                flag_error(hdr, WS_ERR_LOOKBACK_TIMEOUT);
+                flag_error(hdr, WS_ERR_WAIT_TIMEOUT);
             return Codec::identity();  // only reached on a defect; the error word reports it
         }
         __builtin_amdgcn_s_sleep(LB_SLEEP);

@@ -20,17 +20,19 @@ enum Scheme : int {
 };
 
 // ---- single-pass device-wide scan (ls_scan.hip)
-// Zeroes the workspace header and the status word of each of `tiles` tile slots.
-hipError_t clear_workspace(void* ws, int64_t tiles, hipStream_t stream);
+// Zero fill of a workspace of `bytes` bytes (16-byte multiple; the last bytes of
+// any other size are left alone), enqueued on `stream`.
+hipError_t init_workspace(void* ws, size_t bytes, hipStream_t stream);
 int64_t scan_tile_elems();
 size_t scan_workspace_bytes(int64_t n, int scheme);
 hipError_t launch_scan(const void* in, void* out, int64_t n, int dtype, int op, bool inclusive,
                        void* total, void* ws, int scheme, hipStream_t stream);
-// Single-pass exclusive uint32 sum whose workspace header and first
-// scan_sum_u32_tiles(n) status words the caller has zeroed (n >= 1).
+// Single-pass exclusive uint32 sum (n >= 1) on a workspace of
+// scan_workspace_bytes(n, SCHEME_SINGLE_PASS) bytes whose header and first
+// scan_sum_u32_tiles(n) status words are zero (the radix sort zeroes them inside
+// its histogram kernel).
 int64_t scan_sum_u32_tiles(int64_t n);
-hipError_t launch_scan_sum_u32_excl_cleared(const uint32_t* in, uint32_t* out, int64_t n, void* ws,
-                                            hipStream_t stream);
+hipError_t launch_scan_sum_u32_excl(const uint32_t* in, uint32_t* out, int64_t n, void* ws, hipStream_t stream);
 
 // ---- the scan's fixed per-device workspace (ls_noalloc.hip)
 constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(4) << 20;

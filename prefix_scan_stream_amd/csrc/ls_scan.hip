@@ -89,7 +89,48 @@ __device__ __forceinline__ void scan_tile_local(Run4<typename Op::T> (&r)[CHUNKS
 #define LS_SCAN_LDS_RESERVE 0
 #endif
 
-// One tile per block; blocks take tile ids in the order they start.
+// The total of full tile j, computed by one wave with the same operations in the
+// same order as tile j's own block (serial runs of 4, a wave scan over each
+// (run, wave) row of run totals, the parts combined PPL per lane and scanned
+// across one wave), so that float totals match bit for bit.  The fallback of a
+// block-index tile whose wait ran out of time (replay_prefix).
+template <class Op, bool VEC, int CHUNKS>
+__device__ typename Op::T tile_total_by_wave(const typename Op::T* in, int64_t j)
+{
+    using T = typename Op::T;
+    constexpr int PARTS = CHUNKS * SP_WAVES;
+    constexpr int PPL = (PARTS + 63) / 64;
+    constexpr int TILE = SP_BLOCK * CHUNKS * 4;
+    constexpr uint32_t RUN_STRIDE = SP_BLOCK * 16u;
+    const int lane = lane_id();
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + j * TILE, uint32_t(TILE) * 4u);
+    T pv[PPL];
+#pragma unroll
+    for (int q = 0; q < PPL; ++q)
+        pv[q] = Op::identity();
+    for (int c = 0; c < CHUNKS; ++c) {
+        for (int w = 0; w < SP_WAVES; ++w) {
+            const uint32_t voff = uint32_t(w * 64 + lane) * 16u;
+            const Run4<T> r = VEC ? load_run_x4<T>(rin, voff, c * RUN_STRIDE) : load_run_x1<T>(rin, voff, c * RUN_STRIDE);
+            const T v1 = Op::apply(r.v[0], r.v[1]);
+            const T v2 = Op::apply(v1, r.v[2]);
+            const T v3 = Op::apply(v2, r.v[3]);
+            const T part = read_lane(wave_inclusive_scan<Op>(v3), 63);
+            const int p = c * SP_WAVES + w;
+#pragma unroll
+            for (int q = 0; q < PPL; ++q)
+                pv[q] = (PPL * lane + q == p) ? part : pv[q];  // a select: no run-time register index
+        }
+    }
+    T v = Op::identity();
+#pragma unroll
+    for (int q = 0; q < PPL; ++q)
+        v = Op::apply(v, pv[q]);
+    return read_lane(wave_inclusive_scan<Op>(v), 63);
+}
+
+// One tile per block.  The chased scans (BY_INDEX) take tile = block index; the
+// others take tile ids in the order blocks start (tickets).
 // FIXED: the look-back combines a fixed set of words in a fixed order
 // (lookback_grouped), so float results are the same bits on every run.
 template <class Op, bool INCLUSIVE, bool VEC, int CHUNKS, bool FIXED = false>
@@ -99,23 +140,47 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
 {
     using T = typename Op::T;
     using Codec = ScanCodec<Op>;
+    constexpr bool BY_INDEX = !FIXED && sp_chase<Op>;
     constexpr int PARTS = CHUNKS * SP_WAVES;  // (run, wave) partial totals per tile
     constexpr int PPL = (PARTS + 63) / 64;    // partial totals per lane in their scan
     constexpr int TILE = SP_BLOCK * CHUNKS * 4;
     constexpr uint32_t RUN_STRIDE = SP_BLOCK * 16u;
     static_assert(PARTS % PPL == 0 && PARTS / PPL <= 64, "the (run, wave) totals are scanned by one wave");
     __shared__ T s_part[PARTS + LS_SCAN_LDS_RESERVE];
-    __shared__ uint32_t s_tile;
+    __shared__ uint64_t s_ticket;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const T id = Op::identity();
 
-    if (tid == 0)
-        s_tile = take_tile_id(hdr);
-    __syncthreads();
-    const int64_t tile = s_tile;
+    int64_t tile;
+    uint32_t ep = 0;
+    if constexpr (BY_INDEX) {
+        // Thread 0 reads the epoch and the block waits for it before loading: the
+        // loads of all eight waves then start together (measured, int32 scan of
+        // 2^28: 326-327 us, against 334 us with each wave loading at once).
+        tile = blockIdx.x;
+        if (tid == 0)
+            s_ticket = read_epoch(hdr);
+        __syncthreads();
+        ep = uint32_t(s_ticket);
+    } else {
+        if (tid == 0) {
+            const uint64_t tk = take_ticket(hdr);
+            s_ticket = tk;
+            if (ticket_tile(tk) == num_tiles - 1)
+                start_next_epoch(hdr, ticket_epoch(tk));  // the call's last ticket is out
+            else if (ticket_tile(tk) >= num_tiles)
+                flag_error(hdr, WS_ERR_BAD_TICKET);
+        }
+        __syncthreads();
+        const uint64_t ticket = s_ticket;
+        tile = ticket_tile(ticket);
+        ep = ticket_epoch(ticket);
+        if (tile >= num_tiles)
+            return;  // uniform over the block: a workspace that was not initialised
+    }
     const int64_t tbase = tile * TILE;
     const int64_t rem = n - tbase;
     const uint32_t valid = rem < TILE ? uint32_t(rem) : uint32_t(TILE);
@@ -158,26 +223,44 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
             // their totals (read by the later tiles of their group)
             const bool last_of_group = tile % LB_GROUP == LB_GROUP - 1;
             if (lane == 0 && !last_of_group)
-                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
+                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg, ep));
             if (tile != 0)
-                p = lookback_grouped<Codec>(status, tile, hdr);
+                p = lookback_grouped<Codec>(status, tile, ep, hdr);
             if (lane == 0 && last_of_group)
-                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg)));
+                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg), ep));
+        } else if constexpr (BY_INDEX) {
+            if (lane == 0) {
+                status_store(total_word(status, tile), Codec::pack(ST_AGGREGATE, agg, ep));
+                if (tile == 0)
+                    status_store(status, Codec::pack(ST_PREFIX, agg, ep));
+            }
+            bool replayed = false;
+            if (tile == 0) {
+                agg0 = agg;
+            } else if (!wait_prefix<Codec>(status, tile, ep, p)) {
+                // out of time (the tile before may not even have been dispatched):
+                // compute the chasing wave's value here
+                p = replay_prefix<Codec>(status, tile - 1, ep, [&](int64_t j) {
+                    return tile_total_by_wave<Op, VEC, CHUNKS>(in, j);
+                });
+                replayed = true;
+            }
+            if (tile == num_tiles - 1) {  // every block has read the epoch: the next call may start a new one
+                if (replayed)
+                    await_totals<Codec>(status, tile, ep, hdr);
+                if (lane == 0)
+                    start_next_epoch(hdr, ep);
+            }
         } else if (tile == 0) {
             if (lane == 0)
-                status_store(status, Codec::pack(ST_PREFIX, agg));
-            agg0 = agg;
+                status_store(status, Codec::pack(ST_PREFIX, agg, ep));
         } else {
+            // tickets, walking look-back (the affine maps)
             if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg));
-            if constexpr (sp_chase<Op>) {
-                // the chasing wave turns this total into a full prefix
-                p = wait_prefix<Codec>(status, tile, hdr);
-            } else {
-                p = lookback<Codec, SP_LB_WIDE>(status, tile, hdr);
-                if (lane == 0)
-                    status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg)));
-            }
+                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg, ep));
+            p = lookback<Codec, SP_LB_WIDE>(status, tile, ep, hdr);
+            if (lane == 0)
+                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg), ep));
         }
         T e = Op::apply(p, exc);
 #pragma unroll
@@ -225,9 +308,9 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
 
     // 5. tile 0's first wave, its own tile written, publishes every later tile's
     // full prefix (it returns once the last tile's is out)
-    if constexpr (!FIXED && sp_chase<Op>) {
+    if constexpr (BY_INDEX) {
         if (tile == 0 && wave == 0)
-            chase_prefixes<Codec>(status, num_tiles, agg0, hdr);
+            chase_prefixes<Codec>(status, num_tiles, agg0, ep);
     }
 }
 
@@ -416,17 +499,13 @@ __global__ void write_total_kernel(const typename Op::T* seeds, const typename O
         *total = Op::apply(seeds[last], totals[last]);
 }
 
-// Clears the workspace header and the first `words` status words.
-// Zeroes the workspace header and the status word of every tile slot (the rest
-// of a slot is never read).  A kernel, not a memset, so the call can be captured
-// in a graph.
-__global__ __launch_bounds__(256) void ws_clear_kernel(uint32_t* hdr_words, uint64_t* status, int64_t tiles)
+// Zero fill of a workspace (ls_workspace_init): 16-byte stores, a kernel rather
+// than a memset so that the call can be captured in a graph.
+__global__ __launch_bounds__(256) void ws_zero_kernel(u32x4* p, int64_t words)
 {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i < int64_t(sizeof(WsHeader) / 4))
-        hdr_words[i] = 0u;
-    if (i < tiles)
-        status[i * STATUS_STRIDE] = 0u;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < words; i += int64_t(gridDim.x) * 256)
+        p[i] = z;
 }
 
 __global__ void store_u32_kernel(uint32_t* p, uint32_t v)
@@ -468,13 +547,14 @@ size_t scan_workspace_bytes(int64_t n, int scheme)
     return bytes;
 }
 
-hipError_t clear_workspace(void* ws, int64_t tiles, hipStream_t s)
+hipError_t init_workspace(void* ws, size_t bytes, hipStream_t s)
 {
-    const int64_t n = tiles > int64_t(sizeof(WsHeader) / 4) ? tiles : int64_t(sizeof(WsHeader) / 4);
-    const int64_t blocks = (n + 255) / 256;
-    auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
-    hipLaunchKernelGGL(ws_clear_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<uint32_t*>(ws), status, tiles);
+    const int64_t words = int64_t(bytes / 16);
+    if (words == 0)
+        return hipSuccess;
+    int64_t blocks = (words + 255) / 256;
+    blocks = blocks < 1024 ? blocks : 1024;
+    hipLaunchKernelGGL(ws_zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, reinterpret_cast<u32x4*>(ws), words);
     return hipGetLastError();
 }
 
@@ -525,11 +605,8 @@ static void launch_single_pass(const void* in, void* out, int64_t n, int64_t til
 // Tiles (status slots) of the single-pass uint32 sum over n elements.
 int64_t scan_sum_u32_tiles(int64_t n) { return (n + SP_TILE - 1) / SP_TILE; }
 
-// Exclusive uint32 sum by the single pass, for a caller that has already zeroed the
-// workspace header and the first scan_sum_u32_tiles(n) status words (n >= 1): the
-// radix sort does it inside its histogram kernel and so saves a launch per pass.
-hipError_t launch_scan_sum_u32_excl_cleared(const uint32_t* in, uint32_t* out, int64_t n, void* ws,
-                                            hipStream_t s)
+// Exclusive uint32 sum by the single pass (n >= 1), for the radix sort.
+hipError_t launch_scan_sum_u32_excl(const uint32_t* in, uint32_t* out, int64_t n, void* ws, hipStream_t s)
 {
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
@@ -550,9 +627,6 @@ static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive,
     constexpr int CHUNKS = FIXED ? SCAN_CHUNKS : sp_chunks<Op>;
     constexpr int64_t TILE = int64_t(SP_BLOCK) * CHUNKS * 4;
     const int64_t tiles = (n + TILE - 1) / TILE;  // never more than the workspace holds
-    hipError_t e = clear_workspace(ws, tiles, s);
-    if (e != hipSuccess)
-        return e;
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
     launch_single_pass<Op, CHUNKS, FIXED>(in, out, n, tiles, inclusive, total, hdr, status, s);

@@ -104,18 +104,24 @@ __device__ __forceinline__ SegPair<Op> seg_read_lane(SegPair<Op> p, int lane)
     return {read_lane(p.v, lane), read_lane(p.h, lane)};
 }
 
-// Status word of a tile: bits 63..62 status flag, bit 32 head, bits 31..0 value.
+// Status word of a tile: bits 63..62 status flag, bit 61 head, bits 60..32 the
+// call's epoch (29 bits), bits 31..0 value.
 template <class Op>
 struct SegCodec {
     using V = SegPair<Op>;
-    static __device__ __forceinline__ uint32_t flag(uint64_t w) { return uint32_t(w >> 62); }
+    static constexpr uint32_t EPOCH_MASK = (1u << 29) - 1u;
+    static __device__ __forceinline__ uint32_t flag(uint64_t w, uint32_t ep)
+    {
+        return ((uint32_t(w >> 32) & EPOCH_MASK) == (ep & EPOCH_MASK)) ? uint32_t(w >> 62) : ST_EMPTY;
+    }
     static __device__ __forceinline__ V value(uint64_t w)
     {
-        return {from_bits<typename Op::T>(uint32_t(w)), uint32_t(w >> 32) & 1u};
+        return {from_bits<typename Op::T>(uint32_t(w)), uint32_t(w >> 61) & 1u};
     }
-    static __device__ __forceinline__ uint64_t pack(uint32_t f, V p)
+    static __device__ __forceinline__ uint64_t pack(uint32_t f, V p, uint32_t ep)
     {
-        return (uint64_t(f) << 62) | (uint64_t(p.h ? 1u : 0u) << 32) | uint64_t(to_bits(p.v));
+        return (uint64_t(f) << 62) | (uint64_t(p.h ? 1u : 0u) << 61) | (uint64_t(ep & EPOCH_MASK) << 32) |
+               uint64_t(to_bits(p.v));
     }
     static __device__ __forceinline__ V identity() { return seg_identity<Op>(); }
     static __device__ __forceinline__ V apply(V a, V b) { return seg_apply<Op>(a, b); }
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
     static_assert(PARTS % PPL == 0 && PARTS / PPL <= 64, "the (run, wave) pairs are scanned by one wave");
     __shared__ T s_pv[PARTS];
     __shared__ uint32_t s_ph[PARTS];
-    __shared__ uint32_t s_tile;
+    __shared__ uint64_t s_ticket;
     __shared__ int64_t s_k0;
     __shared__ uint32_t s_bits[SRC == SEG_OFFSETS ? SG_TILE / 32 : 1];
 
@@ -153,10 +159,20 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
     const int wave = tid >> 6;
     const T id = Op::identity();
 
-    if (tid == 0)
-        s_tile = take_tile_id(hdr);
+    if (tid == 0) {
+        const uint64_t tk = take_ticket(hdr);
+        s_ticket = tk;
+        if (ticket_tile(tk) == num_tiles - 1)
+            start_next_epoch(hdr, ticket_epoch(tk));  // the call's last ticket is out
+        else if (ticket_tile(tk) >= num_tiles)
+            flag_error(hdr, WS_ERR_BAD_TICKET);
+    }
     __syncthreads();
-    const int64_t tile = s_tile;
+    const uint64_t ticket = s_ticket;
+    const int64_t tile = ticket_tile(ticket);
+    const uint32_t ep = ticket_epoch(ticket);
+    if (tile >= num_tiles)
+        return;  // uniform over the block: a workspace that was not initialised
     const int64_t tbase = tile * SG_TILE;
     const int64_t rem = n - tbase;
     const uint32_t valid = rem < SG_TILE ? uint32_t(rem) : uint32_t(SG_TILE);
@@ -261,16 +277,21 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
         const P exc = seg_wave_shift_up<Op>(inc);
         const P agg = seg_read_lane<Op>(inc, 63);
         P carry = seg_identity<Op>();
+        // every tile publishes its total; tile 0 and tiles containing a head also
+        // their full prefix, which then does not depend on earlier tiles
+        if (lane == 0) {
+            status_store(total_word(status, tile), Codec::pack(ST_AGGREGATE, agg, ep));
+            if (tile == 0 || agg.h)
+                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, agg, ep));
+        }
         if (tile == 0) {
-            if (lane == 0)
-                status_store(status, Codec::pack(ST_PREFIX, agg));
             agg0 = agg;
         } else {
-            if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(agg.h ? ST_PREFIX : ST_AGGREGATE, agg));
             const bool first_is_head = __builtin_amdgcn_readfirstlane(hb[0] & 1u) != 0u;
-            if (!first_is_head)
-                carry = wait_prefix<Codec>(status, tile, hdr);
+            if (!first_is_head && !wait_prefix<Codec>(status, tile, ep, carry)) {
+                if (lane == 0)
+                    flag_error(hdr, WS_ERR_WAIT_TIMEOUT);  // only on a defect: tickets make every wait finite
+            }
         }
         P e = seg_apply<Op>(carry, exc);
 #pragma unroll
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
     // 5. tile 0's first wave, its own tile written, publishes the later tiles' full
     // prefixes (it returns once the last tile's is out)
     if (tile == 0 && wave == 0)
-        chase_prefixes<Codec>(status, (n + SG_TILE - 1) / SG_TILE, agg0, hdr);
+        chase_prefixes<Codec>(status, num_tiles, agg0, ep);
 }
 
 // ------------------------------------------------------------------ host side
@@ -358,9 +379,6 @@ static hipError_t run_segmented(const void* in, void* out, int64_t n, bool excl,
         return hipGetLastError();
     }
     const int64_t tiles = sg_tiles(n);
-    hipError_t e = clear_workspace(ws, tiles, s);
-    if (e != hipSuccess)
-        return e;
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));
     const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;

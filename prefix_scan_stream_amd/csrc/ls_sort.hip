@@ -73,7 +73,8 @@ __device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift)
 constexpr int RS_HT = 4;
 
 // Block 0 also zeroes the workspace header and the `scan_tiles` status words of
-// the scan that follows (a launch fewer per pass).
+// the scan that follows (a launch fewer per pass), so the sort needs nothing
+// from its workspace's earlier contents.
 template <int DT>
 __global__ __launch_bounds__(RS_BLOCK) void rs_hist_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                            int shift, uint32_t* __restrict__ hist,
@@ -86,10 +87,14 @@ __global__ __launch_bounds__(RS_BLOCK) void rs_hist_kernel(const uint32_t* __res
     const int wave = tid >> 6;
     const int64_t t0 = int64_t(blockIdx.x) * RS_HT;
     if (blockIdx.x == 0) {
-        if (tid < int(sizeof(WsHeader) / 4))
+        // the header's ticket restarts; its error word (word 2) is kept, so that
+        // ls_workspace_check still sees a give-up of an earlier pass
+        if (tid < int(sizeof(WsHeader) / 4) && tid != 2)
             scan_hdr[tid] = 0u;
-        for (int64_t i = tid; i < scan_tiles; i += RS_BLOCK)
-            scan_status[i * STATUS_STRIDE] = 0u;
+        for (int64_t i = tid; i < scan_tiles; i += RS_BLOCK) {
+            scan_status[i * STATUS_STRIDE] = 0u;               // prefix word
+            scan_status[i * STATUS_STRIDE + TOTAL_WORD] = 0u;  // total word
+        }
     }
     for (int i = tid; i < RS_HT * RS_DIGITS; i += RS_BLOCK)
         cnt[i / RS_DIGITS][i % RS_DIGITS] = 0;
@@ -268,11 +273,11 @@ size_t sort_workspace_bytes(int64_t n, bool with_values)
 {
     const int64_t tiles = rs_tiles(n) < 1 ? 1 : rs_tiles(n);
     const int64_t m = int64_t(RS_DIGITS) * tiles;
-    size_t b = rs_round(size_t(n) * 4);              // keys between passes
+    size_t b = rs_round(scan_workspace_bytes(m, SCHEME_SINGLE_PASS));  // the histogram's scan, first
+    b += rs_round(size_t(n) * 4);                    // keys between passes
     if (with_values)
         b += rs_round(size_t(n) * 4);                // values between passes
     b += rs_round(size_t(m) * 4);                    // digit histogram / offsets
-    b += scan_workspace_bytes(m, SCHEME_SINGLE_PASS); // its scan
     return b;
 }
 
@@ -284,6 +289,9 @@ static hipError_t run_sort(const uint32_t* kin, uint32_t* kout, const uint32_t* 
     const int64_t m = int64_t(RS_DIGITS) * tiles;
     const bool vals = vin != nullptr;
     char* p = ws;
+    void* scan_ws = p;  // first: its header's error word is the workspace's (ls_workspace_check)
+    auto* scan_status = reinterpret_cast<uint64_t*>(p + sizeof(WsHeader));
+    p += rs_round(scan_workspace_bytes(m, SCHEME_SINGLE_PASS));
     uint32_t* tk = reinterpret_cast<uint32_t*>(p);
     p += rs_round(size_t(n) * 4);
     uint32_t* tv = nullptr;
@@ -292,10 +300,7 @@ static hipError_t run_sort(const uint32_t* kin, uint32_t* kout, const uint32_t* 
         p += rs_round(size_t(n) * 4);
     }
     uint32_t* hist = reinterpret_cast<uint32_t*>(p);
-    p += rs_round(size_t(m) * 4);
-    void* scan_ws = p;
-    auto* scan_status = reinterpret_cast<uint64_t*>(p + sizeof(WsHeader));
-    const int64_t scan_tiles = scan_sum_u32_tiles(m);
+    const int64_t scan_tiles = scan_sum_u32_tiles(m);  // status words the scan reads
     const dim3 grid(static_cast<uint32_t>(tiles)), block(RS_BLOCK);
     const dim3 hgrid(static_cast<uint32_t>((tiles + RS_HT - 1) / RS_HT));
     const uint32_t* sk = kin;
@@ -306,7 +311,7 @@ static hipError_t run_sort(const uint32_t* kin, uint32_t* kout, const uint32_t* 
         uint32_t* dv = (pass % 2 == 0) ? tv : vout;
         hipLaunchKernelGGL((rs_hist_kernel<DT>), hgrid, block, 0, s, sk, n, shift, hist, tiles,
                            reinterpret_cast<uint32_t*>(scan_ws), scan_status, scan_tiles);
-        hipError_t e = launch_scan_sum_u32_excl_cleared(hist, hist, m, scan_ws, s);
+        hipError_t e = launch_scan_sum_u32_excl(hist, hist, m, scan_ws, s);
         if (e != hipSuccess)
             return e;
         if (vals)

@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: move seeded numpy inputs to cuda:0 and back,
-and read the error word that the library's look-back leaves in its workspace."""
+and read the error word that the library's bounded waits leave in its workspace."""
 import numpy as np
 import torch
 
@@ -18,11 +18,9 @@ def to_host(t: torch.Tensor) -> np.ndarray:
 
 
 def ws_error_word() -> int:
-    """Error bits of the last call that used the current stream's workspace
-    (0 = clean; 1 = a look-back gave up waiting)."""
-    torch.cuda.synchronize()
-    ws = ps.workspace_for(DEV, torch.cuda.current_stream(DEV), 0)
-    return int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+    """Error bits of the current stream's cached workspace, read through the C ABI
+    (ls_workspace_check): 0 when no call on it gave up a bounded wait."""
+    return ps.workspace_error_flags(DEV)
 
 
 def bits(a) -> np.ndarray:

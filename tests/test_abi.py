@@ -60,8 +60,8 @@ def test_bounded_wait_test_library_exports_the_same_entry_points():
 
 
 def test_version_and_status_strings(lib):
-    assert ps.ls_abi_version() == ps.ABI_VERSION == 4
-    for s in range(5):
+    assert ps.ls_abi_version() == ps.ABI_VERSION == 5
+    for s in range(6):
         assert ps.ls_status_string(s).startswith("LS_")
     assert "unknown" in ps.ls_status_string(99)
 
@@ -122,6 +122,34 @@ def test_scan_validation(lib, fn):
     # error precedence: invalid argument before unsupported before workspace
     assert _scan(lib, fn, None, A_OUT, 10, t=F32, op=XOR, ws=None) == INV
     assert _scan(lib, fn, A_IN, A_OUT, 10, t=F32, op=XOR, ws=None) == UNS
+
+
+def test_workspace_init_and_check_validation(lib):
+    """Both reject a bad workspace on the host, before any HIP call."""
+    init, check = lib.ls_workspace_init, lib.ls_workspace_check
+    assert init(None, 4096, None) == INV
+    assert init(A_WS + 8, 4096, None) == INV      # misaligned
+    assert init(A_WS, 4100, None) == INV          # not a multiple of 16
+    assert init(A_WS, 128, None) == INV           # smaller than the 256-byte header
+    flags = ctypes.c_uint32(7)
+    assert check(None, ctypes.byref(flags), None) == INV
+    assert check(A_WS + 4, ctypes.byref(flags), None) == INV
+    assert flags.value == 7                        # untouched on error
+    assert ps.ls_status_string(ps.LS_ERR_INCOMPLETE).startswith("LS_ERR_INCOMPLETE")
+
+
+def test_size_limits(lib):
+    """Scans take at most 2^40 elements (32-bit tile ids), compactions 2^36 - 1
+    (36-bit counts); larger sizes are invalid arguments."""
+    sz = ctypes.c_size_t(0)
+    assert lib.ls_scan_workspace_bytes(1 << 40, INT32, SUM, ctypes.byref(sz)) == 0
+    assert lib.ls_scan_workspace_bytes((1 << 40) + 1, INT32, SUM, ctypes.byref(sz)) == INV
+    assert lib.ls_segmented_workspace_bytes((1 << 40) + 1, INT32, SUM, ctypes.byref(sz)) == INV
+    assert lib.ls_compact_workspace_bytes((1 << 36) - 1, INT32, ctypes.byref(sz)) == 0
+    assert lib.ls_compact_workspace_bytes(1 << 36, INT32, ctypes.byref(sz)) == INV
+    far = A_IN - (1 << 44)
+    assert lib.compact_if(A_IN, far, A_TOT, 1 << 36, INT32, 0, 0, A_WS, BIG_WS, None) == INV
+    assert _scan(lib, "scan_inclusive", A_IN, far, (1 << 40) + 1) == INV
 
 
 def test_noalloc_scan_validation(lib):

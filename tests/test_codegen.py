@@ -116,3 +116,11 @@ def test_wide_stores_keep_their_data_wait_state(asm, src):
         if nxt.startswith("v_"):
             dst = nxt.split(None, 1)[1].split(",")[0].strip()
             assert not (_vregs(dst) & data), f"{src}: '{line}' then '{nxt}'"
+
+
+@pytest.mark.parametrize("src", [s for s in SOURCES if s != "ls_ceiling.hip"])
+def test_no_cache_writeback_or_invalidate(asm, src):
+    """Tile hand-off uses relaxed device-coherent loads and stores only.  A release
+    or acquire at device scope would add an L2 writeback (buffer_wbl2) or invalidate
+    (buffer_inv); one per block once made the 2^28 scan 2.5 times slower."""
+    assert not re.search(r"\bbuffer_(wbl2|inv)\b", asm[src])

@@ -1,6 +1,6 @@
 """The library's calls can be captured in a HIP graph and replayed.
 
-A call launches only kernels (its workspace is cleared by a kernel, not a memset),
+A call launches only kernels (a workspace is zero-filled by a kernel, not a memset),
 so torch.cuda.graph can capture it.  The graph is replayed several times with eager
 work by the library in between (other inputs, the same entry points), and every
 replay is compared element by element with the result of an eager call."""
@@ -68,4 +68,31 @@ def test_replays_match_eager_calls():
         # eager calls between replays, on other data
         ps.scan_exclusive(other, "sum")
         ps.compact_if(other, "lt", 8)
+        torch.cuda.synchronize()
+
+
+def test_earlier_graph_survives_a_larger_capture():
+    """Two captures on the same (default capture) stream, the second larger: the
+    binding grows that stream's workspace for the second but keeps the first
+    graph's, so replaying the first after the second still matches eager calls."""
+    small = to_dev(wl.int_uniform(3 * 26624 + 5, 0, 16, seed=960))
+    big = to_dev(wl.int_uniform(700 * 26624 + 7, 0, 16, seed=961))
+    want_s = to_host(ps.scan_exclusive(small, "sum"))
+    want_b = to_host(ps.scan_exclusive(big, "sum"))
+    ys, yb = torch.empty_like(small), torch.empty_like(big)
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        ps.scan_exclusive(small, "sum", out=ys)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        ps.scan_exclusive(big, "sum", out=yb)
+    for rep in range(3):
+        ys.fill_(-1)
+        yb.fill_(-1)
+        g2.replay()
+        g1.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(yb), want_b), f"replay {rep}: larger graph"
+        assert np.array_equal(to_host(ys), want_s), f"replay {rep}: earlier graph"
+        ps.scan_exclusive(big, "sum")  # eager work in between
         torch.cuda.synchronize()
