@@ -494,6 +494,8 @@ struct ScanCodec {
     }
     static __device__ __forceinline__ V identity() { return Op::identity(); }
     static __device__ __forceinline__ V apply(V a, V b) { return Op::apply(a, b); }
+    // whether a tile with this total publishes its full prefix itself
+    static __device__ __forceinline__ bool self_published(V) { return false; }
     static __device__ __forceinline__ V wave_scan(V v) { return wave_inclusive_scan<Op>(v); }
     static __device__ __forceinline__ V lane(V v, int l) { return read_lane(v, l); }
     // Combine the lanes' partials in lane order (lanes below `hi` hold identity).
@@ -520,6 +522,7 @@ struct CountCodec {
     }
     static __device__ __forceinline__ V identity() { return 0; }
     static __device__ __forceinline__ V apply(V a, V b) { return a + b; }
+    static __device__ __forceinline__ bool self_published(V) { return false; }
     // The chasing wave scans tile totals (each at most one tile, so 64 of them
     // fit in 32 bits) and adds the 64-bit base afterwards.
     static __device__ __forceinline__ V wave_scan(V v) { return wave_inclusive_scan<SumU32>(uint32_t(v)); }
@@ -700,7 +703,8 @@ __device__ bool wait_prefix(const uint64_t* status, int64_t tile, uint32_t ep, t
 // every run (MI355X, float32 sum of 2^26: one distinct result in 10 runs, against
 // 10 in 10 for windows that start at the frontier, at the same speed).  A tile
 // whose full prefix does not depend on earlier tiles (a segmented tile containing a
-// head) may publish it itself: the wave's scan gives the same value there.
+// head) publishes it itself (Codec::self_published tells from its total); the
+// wave's scan gives the same value there, and the wave does not write it again.
 // A wait without progress past the time limit ends the wave silently: waiting
 // tiles then run out of time themselves and either replay (block-index tiles) or
 // report it (tickets).
@@ -732,7 +736,7 @@ __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Cod
             tot = Codec::value(w);
         // older on the left: base (+) totals of tiles g0 .. g0 + lane
         const V inc = Codec::apply(base, Codec::wave_scan(lane < k ? tot : Codec::identity()));
-        if (lane >= have && lane < k)
+        if (lane >= have && lane < k && !Codec::self_published(tot))
             status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc, ep));
         have = k;
         if (have == 64) {

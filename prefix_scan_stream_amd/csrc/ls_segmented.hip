@@ -125,6 +125,8 @@ struct SegCodec {
     }
     static __device__ __forceinline__ V identity() { return seg_identity<Op>(); }
     static __device__ __forceinline__ V apply(V a, V b) { return seg_apply<Op>(a, b); }
+    // a tile that contains a head publishes its full prefix itself
+    static __device__ __forceinline__ bool self_published(V p) { return p.h != 0u; }
     static __device__ __forceinline__ V wave_reduce(V part, int /*hi*/)
     {
         return seg_read_lane<Op>(seg_wave_inclusive_scan<Op>(part), 63);
