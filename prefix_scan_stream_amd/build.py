@@ -102,7 +102,7 @@ def build_ceiling_lib(verbose: bool = False) -> str:
 
 def build_bounded_wait_test_lib(verbose: bool = False) -> str:
     """libscan_spin1.so: bounded waits give up after one empty poll (test use only)."""
-    return build(verbose, SPIN1_LIB, os.path.join(BUILD, "spin1"), ("-DLS_WAIT_LIMIT_TICKS=0",))
+    return build(verbose, SPIN1_LIB, os.path.join(BUILD, "spin1"), ("-DLS_WAIT_LIMIT_TICKS=0", "-DLS_FALLBACK_TICKS=0"))
 
 
 if __name__ == "__main__":

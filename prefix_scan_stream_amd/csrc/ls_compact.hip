@@ -31,10 +31,10 @@ constexpr int CP_BLOCK = LS_CP_BLOCK;               // data threads per block
 constexpr int CP_WAVES = CP_BLOCK / 64;             // data waves
 constexpr int CP_THREADS = CP_BLOCK + 64;           // data waves + one control wave
 #ifndef LS_CP_CHUNKS
-#define LS_CP_CHUNKS 16
+#define LS_CP_CHUNKS 8
 #endif
 constexpr int CP_CHUNKS = LS_CP_CHUNKS;             // 16-byte runs per data thread
-constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;   // 32768 elements (128 KiB staged in LDS) by default
+constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;   // 16384 elements (64 KiB staged in LDS) by default
 constexpr int CP_LB_WIDE = 8;                       // status words per look-back poll
 
 // Predicate through a 4-entry truth table indexed by the comparison outcome:
@@ -236,7 +236,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
         }
     };
 
-    // Recount of full tile j by the control wave: the fallback of a look-back that
+    // Recount of full tile j by the control wave, for the fallback of a wait that
     // runs out of time (the tile's block may not have been dispatched yet).  A count
     // of kept elements does not depend on the order in which it is summed.
     auto recount = [&](int64_t j) -> uint64_t {
@@ -267,16 +267,16 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
         return uint64_t(read_lane(wave_inclusive_scan<SumU32>(c), 63));
     };
 
-    // prologue: the block's first tile (its block index), counted.  Tiles go to
-    // blocks by index: block b handles b, b + G, b + 2G, ... for G blocks.
+    // Tiles go to the G blocks by index: block b handles tiles b, b + G, b + 2G, ...
+    // Prologue: the first one, counted.
     if (tid == 0) {
         s_arrive = 0;
-        s_next[1] = blockIdx.x;
         s_ep = read_epoch(hdr);
     }
     __syncthreads();
     const uint32_t ep = s_ep;
-    int64_t cur = s_next[1];
+    const int64_t nblk = gridDim.x;
+    int64_t cur = blockIdx.x;
     if (cur >= num_tiles) {  // never with the launch's grid; uniform over the block
         if (tid == 0)
             mark_started(hdr);
@@ -288,7 +288,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
             load_run(cur, j);
         count_tile(cur, 0);
         if (tid == 0) {
-            s_next[0] = cur + gridDim.x;
+            s_next[0] = cur + nblk;
             mark_started(hdr);  // the epoch read completed before the barrier above (its LDS copy)
         }
     }
@@ -319,7 +319,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
                 }
             };
             if (next < num_tiles) {
-                const int64_t g = next + gridDim.x;  // the block's tile after next
+                const int64_t g = next + nblk;  // the block's tile after next
 #pragma unroll
                 for (int j = 0; j < CP_CHUNKS; ++j) {
                     stage_run(j);
@@ -334,6 +334,8 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
                     stage_run(j);
             }
         } else {
+            // the tile's place in the output: the kept elements of all earlier
+            // tiles, by look-back (missing counts recounted here when out of time)
             int64_t base = 0;
             if (cur != 0) {
                 base = int64_t(lookback<CountCodec, CP_LB_WIDE>(status, cur, ep, hdr, recount));
@@ -440,12 +442,25 @@ static uint32_t resident_blocks()
     int v = cacheable ? __atomic_load_n(&cached[dev], __ATOMIC_RELAXED) : 0;
     if (v == 0) {
         int cus = 0, per_cu = 0;
+        hipFuncAttributes attr{};
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 int(CP_TILE * sizeof(uint32_t))) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, CP_THREADS, CP_TILE * sizeof(uint32_t)) !=
-                hipSuccess)
+                hipSuccess ||
+            hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) != hipSuccess)
             return 0;
+        // The occupancy query assumes a block's waves spread evenly over the four
+        // SIMDs of a CU; placed unevenly, a block of CP_THREADS / 64 waves may take
+        // ceil(waves / 4) slots of one SIMD.  Only as many blocks as fit that way
+        // are counted, so that every block of the grid is resident at once (a
+        // block that is not would leave the tiles after its own waiting on the
+        // fallback).  Measured: flag compaction at 96 VGPRs (5 waves per SIMD)
+        // had only 510 of 512 two-per-CU blocks resident.
+        const int vgprs = attr.numRegs > 0 ? (attr.numRegs + 7) & ~7 : 512;
+        const int per_simd = 512 / vgprs < 8 ? 512 / vgprs : 8;
+        const int uneven = per_simd / ((CP_THREADS / 64 + 3) / 4);
+        per_cu = per_cu < uneven ? per_cu : uneven;
         v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
         if (cacheable)
             __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
@@ -462,6 +477,8 @@ static hipError_t launch_compact_kernel(hipStream_t s, const uint32_t* in, uint3
     const uint32_t cap = resident_blocks<DT, VEC, SRC, PAY, FLAG4>();
     if (cap == 0)
         return hipErrorInvalidConfiguration;
+    // at most as many blocks as are resident at once, so that none waits for a tile
+    // whose block cannot start
     const uint32_t grid = tiles < int64_t(cap) ? uint32_t(tiles) : cap;
     hipLaunchKernelGGL(k, dim3(grid), dim3(CP_THREADS), CP_TILE * sizeof(uint32_t), s, in, out, n, tiles, thr,
                        table, hdr, status, count, flags);

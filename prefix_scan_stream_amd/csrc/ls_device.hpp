@@ -361,22 +361,33 @@ __device__ __forceinline__ uint64_t status_load(const uint64_t* p)
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded waiting: a wait that sees no progress for about one second (the
-// wall clock runs at 100 MHz on MI355X) gives up and records the fact in the
-// workspace error word, so a defect can never hang the GPU.  In a correct run a
-// wait lasts microseconds.  A test build sets the limit to 0: every wait then
-// gives up after its first empty poll.
+// Bounded waiting, on the wall clock (100 MHz on MI355X).  In a correct run a wait
+// for another tile lasts microseconds.
+//   A wait that can only give up (ticket tiles, and the chasing wave) does so
+//   after about one second without progress and records it in the workspace
+//   error word, so a defect can never hang the GPU.
+//   A wait with a fallback (block-index tiles) stops after about a millisecond
+//   and computes what it waited for itself: the tile it waits for may belong to
+//   a block that is not resident yet.
+// A test build sets both limits to 0: every wait then stops at its first empty poll.
 #ifndef LS_WAIT_LIMIT_TICKS
 #define LS_WAIT_LIMIT_TICKS 100000000ull
 #endif
+#ifndef LS_FALLBACK_TICKS
+#define LS_FALLBACK_TICKS 100000ull
+#endif
 constexpr uint64_t WAIT_LIMIT_TICKS = LS_WAIT_LIMIT_TICKS;
+constexpr uint64_t FALLBACK_TICKS = LS_FALLBACK_TICKS;
 constexpr uint32_t WS_ERR_WAIT_TIMEOUT = 1u;  // a wait gave up: that call's output is incomplete
 constexpr uint32_t WS_ERR_BAD_TICKET = 2u;    // a tile id past the call's tiles (workspace not initialised,
                                               // or shared by calls that overlap)
 
 // Start of a wait, and whether its time is up (read only after an empty poll).
 __device__ __forceinline__ uint64_t wait_start() { return wall_clock64(); }
-__device__ __forceinline__ bool wait_expired(uint64_t start) { return wall_clock64() - start >= WAIT_LIMIT_TICKS; }
+__device__ __forceinline__ bool wait_expired(uint64_t start, uint64_t limit = WAIT_LIMIT_TICKS)
+{
+    return uint64_t(wall_clock64()) - start >= limit;
+}
 
 // Workspace header (first 256 bytes of every workspace).  A workspace starts
 // zero-filled (ls_workspace_init) and every call leaves it ready for the next:
@@ -384,7 +395,7 @@ __device__ __forceinline__ bool wait_expired(uint64_t start) { return wall_clock
 struct WsHeader {
     uint64_t ticket;       // bits 63..32: the current call's epoch; bits 31..0: tickets handed out so far
     uint32_t error_flags;  // WS_ERR_* bits, kept until the workspace is initialised again
-    uint32_t started;      // block-index kernels: blocks that have read the current epoch
+    uint32_t started;      // the compaction: blocks that have read the current epoch
     uint32_t pad[60];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
@@ -412,54 +423,52 @@ __device__ __forceinline__ uint64_t take_ticket(WsHeader* h)
 }
 
 // Block index (the plain single-pass scan and the compaction): tile = the block's
-// index, which costs no atomic at the start of a block (one device-scope atomic on
-// one address serializes at about 12 ns on MI355X, which is most of the gap
-// between a tiled copy and the scan).  Without tickets, a tile may wait for a tile
-// whose block has not been dispatched, so every such wait has a fallback that
-// needs no other block: after a time limit the waiting tile computes what it
-// waits for from the input itself (ls_device.hpp: replay_prefix, and the
-// recounting look-back of the compaction).  The call's epoch is read from the
-// header by each block's thread 0, which then counts the block as started; the
-// block that finishes the call's last tile waits until every block has started
-// (so none can read the epoch afterwards) and then starts the next epoch.
+// index (the compaction's persistent blocks: every G-th tile from it), which
+// costs no atomic at the start of a block (one device-scope atomic on one address
+// serializes at about 12 ns on MI355X, which is most of the gap between a tiled
+// copy and the scan).  Without tickets, a tile may wait for a tile whose block
+// has not been dispatched, so every such wait has a fallback that needs no other
+// block: after FALLBACK_TICKS the waiting tile computes what it waits for from
+// the input itself (replay_prefix below; the compaction's recounting look-back).
+// The call's epoch is read from the header at each block's start.  The block
+// that finishes the call's last tile starts the next epoch once no block can
+// still read the old one.  In the scan: when its prefix came from the chasing
+// wave, that wave had seen the totals of every earlier tile, each written by its
+// own block after reading the epoch, so every block had started; when it
+// computed its prefix itself, it first waits until every earlier tile's own block
+// has published its total (await_totals).  The compaction counts started blocks
+// (mark_started, end_call below).
 __device__ __forceinline__ uint32_t read_epoch(WsHeader* h)
 {
     return ticket_epoch(__hip_atomic_load(&h->ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
-// Once per block, by the thread that read the epoch, after it has stored
-// something computed from the epoch: that store waits for the read, so the read
-// is complete before this count is issued.  The count itself is relaxed: a
-// release here would write back the L2 of the XCD for every block (measured: the
-// scan of 2^28 at 831 instead of 325 us).  Nothing waits for its result.
+
+// await_totals waits for blocks that will certainly run (each starts as soon as
+// others finish); its limit only guards against defects.
+constexpr uint64_t AWAIT_LIMIT_TICKS = 1000000000ull;  // about 10 s
+
+__device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits);
+
+// The compaction's walking look-back does not tell the last tile whether every
+// block has read the epoch (a recounted tile's block may not have started), so
+// its blocks are counted instead: thread 0 of each block counts its block as
+// started once it has used the epoch (a store of a value computed from it, or an
+// LDS copy behind a barrier, has made the read complete; the count is relaxed: a
+// release would write back the L2 of the XCD, about 1.5 us per block).  The block
+// that finishes the last tile waits until all have started, then starts the next
+// epoch.  A late block is one that waits for a slot, which frees as others finish.
 __device__ __forceinline__ void mark_started(WsHeader* h)
 {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keeps the compiler from issuing it earlier
     __hip_atomic_fetch_add(&h->started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A wait that always ends in a correct run (the blocks it waits for start as soon
-// as others finish); its limit only guards against defects.
-constexpr uint64_t END_CALL_LIMIT_TICKS = 100000000ull;
-
-// The chased scan needs no count of started blocks: if the call's last tile
-// obtained its prefix from the chasing wave, that wave had seen the totals of
-// all earlier tiles, each written by its own block after reading the epoch, so
-// every block has started.  Only a last tile that replayed its prefix must first
-// see every earlier total word published (await_totals) before starting the next
-// epoch.  Called by one whole wave.
-
-__device__ __forceinline__ void flag_error(WsHeader* h, uint32_t bits);
-
-// By one thread of the block that finished the call's last tile, after its own
-// mark_started.  In the usual case every block started long before, because the
-// last tile's prefix needed every other tile's total.
 __device__ __forceinline__ void end_call(WsHeader* h, uint32_t epoch, uint32_t blocks)
 {
     const uint64_t t0 = wall_clock64();
-    // relaxed: the epoch store below depends on this loop's exit, so it is issued
-    // only after the count was seen complete
+    // relaxed: the epoch store below is issued only after this loop has exited
     while (__hip_atomic_load(&h->started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < blocks) {
-        if (uint64_t(wall_clock64()) - t0 >= END_CALL_LIMIT_TICKS) {
+        if (uint64_t(wall_clock64()) - t0 >= AWAIT_LIMIT_TICKS) {
             flag_error(h, WS_ERR_WAIT_TIMEOUT);
             break;
         }
@@ -605,7 +614,7 @@ __device__ typename Codec::V lookback(const uint64_t* status, int64_t tile, uint
         const int hi = has ? 63 - __builtin_clzll(has) : -1;
         uint64_t empty = __ballot(act && lane > hi && Codec::flag(w, ep) == ST_EMPTY);
         if (empty) {
-            if (!wait_expired(t0)) {
+            if (!wait_expired(t0, __is_same(Recount, NoRecount) ? WAIT_LIMIT_TICKS : FALLBACK_TICKS)) {
                 __builtin_amdgcn_s_sleep(LB_SLEEP);
                 continue;
             }
@@ -675,7 +684,8 @@ __device__ __forceinline__ uint64_t* total_word(uint64_t* status, int64_t tile)
 // `tile`.  Called by a whole wave; every lane reads the same word.  Returns false
 // when the time limit passes first (`out` is then untouched).
 template <class Codec>
-__device__ bool wait_prefix(const uint64_t* status, int64_t tile, uint32_t ep, typename Codec::V& out)
+__device__ bool wait_prefix(const uint64_t* status, int64_t tile, uint32_t ep, typename Codec::V& out,
+                            uint64_t limit)
 {
     const uint64_t* p = status + (tile - 1) * STATUS_STRIDE;
     const uint64_t t0 = wait_start();
@@ -685,7 +695,7 @@ __device__ bool wait_prefix(const uint64_t* status, int64_t tile, uint32_t ep, t
             out = Codec::value(w);
             return true;
         }
-        if (wait_expired(t0))
+        if (wait_expired(t0, limit))
             return false;
         __builtin_amdgcn_s_sleep(LB_WAIT_SLEEP);
     }
@@ -708,23 +718,45 @@ __device__ bool wait_prefix(const uint64_t* status, int64_t tile, uint32_t ep, t
 // A wait without progress past the time limit ends the wave silently: waiting
 // tiles then run out of time themselves and either replay (block-index tiles) or
 // report it (tickets).
-template <class Codec>
-__device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V total0, uint32_t ep)
+// have0 = 1: lane 0 starts with tile 0's total (total0, the caller's own tile);
+// have0 = 0: tile 0's total is polled like the others (total0 unused).
+// AHEAD = 2: each poll also reads the next group's 64 total words (a second word
+// per lane), so one poll can carry the frontier over up to 128 tiles.  The
+// compaction needs it: its 16384-element tiles come at about 80 per microsecond,
+// more than one group per poll round trip (about a microsecond) can follow.  The
+// groups and their scans stay those of tile 0's alignment, so the values do not
+// change with AHEAD.
+template <class Codec, int AHEAD = 1>
+__device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Codec::V total0, uint32_t ep,
+                               int have0 = 1)
 {
+    static_assert(AHEAD == 1 || AHEAD == 2, "one or two groups per poll");
     using V = typename Codec::V;
     const int lane = lane_id();
     int64_t g0 = 0;                                  // first tile of the current group
     V base = Codec::identity();                      // full prefix of tile g0 - 1
-    V tot = lane == 0 ? total0 : Codec::identity();  // totals of the group's tiles seen so far
-    int have = 1;                                    // lanes 0 .. have-1 hold their totals
+    V tot[AHEAD];                                    // totals seen so far: group g0 (+ the next)
+#pragma unroll
+    for (int q = 0; q < AHEAD; ++q)
+        tot[q] = Codec::identity();
+    if (lane == 0 && have0)
+        tot[0] = total0;
+    int have = have0;                                // tiles g0 .. g0 + have - 1 hold their totals
     uint64_t t0 = wait_start();
     while (g0 + have < num_tiles) {
-        const int64_t idx = g0 + lane;
-        const bool want = lane >= have && idx < num_tiles;
-        const uint64_t w = want ? status_load(total_word(status, idx)) : 0ull;
-        const bool ready = lane < have || (want && Codec::flag(w, ep) == ST_AGGREGATE);
-        const uint64_t miss = __ballot(!ready);
-        const int k = miss ? __builtin_ctzll(miss) : 64;  // lanes 0 .. k-1 now hold totals
+        uint64_t w[AHEAD];
+        int k = 64 * AHEAD;                          // tiles g0 .. g0 + k - 1 now hold totals
+#pragma unroll
+        for (int q = 0; q < AHEAD; ++q) {
+            const int pos = 64 * q + lane;
+            const int64_t idx = g0 + pos;
+            const bool want = pos >= have && idx < num_tiles;
+            w[q] = want ? status_load(total_word(status, idx)) : 0ull;
+            const bool ready = pos < have || (want && Codec::flag(w[q], ep) == ST_AGGREGATE);
+            const uint64_t miss = __ballot(!ready);
+            if (miss && k == 64 * AHEAD)
+                k = 64 * q + __builtin_ctzll(miss);
+        }
         if (k == have) {
             if (wait_expired(t0))
                 return;
@@ -732,18 +764,31 @@ __device__ void chase_prefixes(uint64_t* status, int64_t num_tiles, typename Cod
             continue;
         }
         t0 = wait_start();
-        if (lane >= have && lane < k)
-            tot = Codec::value(w);
-        // older on the left: base (+) totals of tiles g0 .. g0 + lane
-        const V inc = Codec::apply(base, Codec::wave_scan(lane < k ? tot : Codec::identity()));
-        if (lane >= have && lane < k && !Codec::self_published(tot))
-            status_store(status + idx * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc, ep));
+        V b = base;
+#pragma unroll
+        for (int q = 0; q < AHEAD; ++q) {
+            const int pos = 64 * q + lane;
+            if (pos >= have && pos < k)
+                tot[q] = Codec::value(w[q]);
+            if (64 * q < k) {
+                // older on the left: b (+) totals of the group's tiles up to this lane
+                const int kq = k - 64 * q < 64 ? k - 64 * q : 64;
+                const V inc = Codec::apply(b, Codec::wave_scan(lane < kq ? tot[q] : Codec::identity()));
+                if (pos >= have && pos < k && !Codec::self_published(tot[q]))
+                    status_store(status + (g0 + pos) * STATUS_STRIDE, Codec::pack(ST_PREFIX, inc, ep));
+                if (kq == 64)
+                    b = Codec::lane(inc, 63);
+            }
+        }
         have = k;
-        if (have == 64) {
-            base = Codec::lane(inc, 63);
+        while (have >= 64) {  // group g0 complete: slide by one group
+            base = Codec::lane(Codec::apply(base, Codec::wave_scan(tot[0])), 63);
             g0 += 64;
-            have = 0;
-            tot = Codec::identity();
+            have -= 64;
+#pragma unroll
+            for (int q = 0; q + 1 < AHEAD; ++q)
+                tot[q] = tot[q + 1];
+            tot[AHEAD - 1] = Codec::identity();
         }
     }
 }
@@ -803,7 +848,7 @@ __device__ typename Codec::V replay_prefix(uint64_t* status, int64_t last, uint3
 }
 
 // Waits until tiles 0 .. last-1 have each published their own total under epoch
-// `ep` (see end of call above).  One whole wave; bounded like end_call.
+// `ep` (see the block-index tiles above).  One whole wave.
 template <class Codec>
 __device__ void await_totals(uint64_t* status, int64_t last, uint32_t ep, WsHeader* hdr)
 {
@@ -814,7 +859,7 @@ __device__ void await_totals(uint64_t* status, int64_t last, uint32_t ep, WsHead
             const bool ok = idx >= last || Codec::flag(status_load(total_word(status, idx)), ep) == ST_AGGREGATE;
             if (!__ballot(!ok))
                 break;
-            if (uint64_t(wall_clock64()) - t0 >= END_CALL_LIMIT_TICKS) {
+            if (uint64_t(wall_clock64()) - t0 >= AWAIT_LIMIT_TICKS) {
                 if (lane_id() == 0)
                     flag_error(hdr, WS_ERR_WAIT_TIMEOUT);
                 return;

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
             bool replayed = false;
             if (tile == 0) {
                 agg0 = agg;
-            } else if (!wait_prefix<Codec>(status, tile, ep, p)) {
+            } else if (!wait_prefix<Codec>(status, tile, ep, p, FALLBACK_TICKS)) {
                 // out of time (the tile before may not even have been dispatched):
                 // compute the chasing wave's value here
                 p = replay_prefix<Codec>(status, tile - 1, ep, [&](int64_t j) {

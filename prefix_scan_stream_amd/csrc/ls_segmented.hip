@@ -290,7 +290,7 @@ __global__ __launch_bounds__(SG_BLOCK) void seg_scan_kernel(const typename Op::T
             agg0 = agg;
         } else {
             const bool first_is_head = __builtin_amdgcn_readfirstlane(hb[0] & 1u) != 0u;
-            if (!first_is_head && !wait_prefix<Codec>(status, tile, ep, carry)) {
+            if (!first_is_head && !wait_prefix<Codec>(status, tile, ep, carry, WAIT_LIMIT_TICKS)) {
                 if (lane == 0)
                     flag_error(hdr, WS_ERR_WAIT_TIMEOUT);  // only on a defect: tickets make every wait finite
             }

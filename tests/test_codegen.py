@@ -77,7 +77,7 @@ def kernel_body(text, mangled_prefix):
     ("ls_scan.hip", "_ZN2ls18tile_reduce_kernelINS_6SumU32ELb1E", 16),
     ("ls_scan.hip", "_ZN2ls16tile_scan_kernelINS_6SumU32ELb0ELb1E", 16),
     ("ls_scan.hip", "_ZN2ls17add_offset_kernelINS_6SumU32ELb1E", 16),
-    ("ls_compact.hip", "_ZN2ls14compact_kernelILi0ELb1E", 16),
+    ("ls_compact.hip", "_ZN2ls14compact_kernelILi0ELb1E", 8),
 ])
 def test_aligned_tiles_load_128_bits(asm, src, prefix, runs):
     """Aligned tiles are read with 128-bit loads only (one per run of 4 elements; the
