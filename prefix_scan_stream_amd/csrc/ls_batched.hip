@@ -86,8 +86,12 @@ constexpr int ROWB_CHUNK = ROWB_BLOCK * 4;
 //   BS_HS_DOUBLE   Hillis-Steele with two LDS buffers, one barrier per step
 //                  (same section, the double-buffer form);
 //   BS_BLELLOCH    up-sweep, cleared root, down-sweep over LDS, 2 x 8 + 1
-//                  barriers, indices padded by one word per 32 against LDS bank
-//                  conflicts (geek-doc.cn section 三; pgsm.cn section 5.4).
+//                  barriers (geek-doc.cn section 三; pgsm.cn section 5.4).  The
+//                  pair indices ai = offset (2 tid + 1) - 1, bi = offset (2 tid + 2) - 1
+//                  at each level follow the pseudo-code of the lpnh.cn parallel scan
+//                  overview, section 2.3; here every index is padded by one word per
+//                  32, which leaves each level's active lanes on distinct LDS banks
+//                  (rocprofv3 SQ_LDS_BANK_CONFLICT reads 0 for all four variants).
 enum BlockScanKind : int { BS_WAVE_DPP = 0, BS_HS = 1, BS_HS_DOUBLE = 2, BS_BLELLOCH = 3 };
 
 template <class Op, int KIND>
