@@ -153,7 +153,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--legs", default=",".join(DEFAULT_LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -355,10 +355,10 @@ def main():
             ms = timer.run(lambda i, v=v: ps.radix_sort(keys, v, out_keys=ok_,
                                                         out_values=ov_ if v is not None else None), K, W)
             moved = 4 * per_pass * n
-            result_legs[name] = {"us": round(ms * 1e3, 1), "gkeys_s": round(n / ms / 1e6, 2),
+            result_legs[name] = {"us": round(ms * 1e3, 1), **timer.spread(), "gkeys_s": round(n / ms / 1e6, 2),
                                  "moved_gbs": round(moved / (ms * 1e-3) / 1e9, 1),
                                  "bytes_moved_per_key": 4 * per_pass}
-            log(f"{name}: {ms * 1e3:.1f} us, {n / ms / 1e6:.2f} Gkeys/s")
+            log(f"{name}: {ms * 1e3:.1f} us (median {timer.spread()['us_median']}), {n / ms / 1e6:.2f} Gkeys/s")
         del keys, vals, ok_, ov_
     if "ceiling" in legs:
         # plain read / write / copy kernels over the headline's bytes (1 GiB each way):
