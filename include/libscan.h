@@ -248,7 +248,7 @@ ls_status scan_ex(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, in
 /* scan_inclusive / scan_exclusive for callers that cannot allocate device memory
  * at the point of the call: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  It takes no workspace: the library keeps a
- * fixed 4 MiB array in device memory per GPU (held until the process ends) and
+ * fixed 8 MiB array in device memory per GPU (held until the process ends) and
  * uses it as the single-pass scan's workspace; the call itself allocates and frees
  * nothing.  The first call on a device looks the array up and enqueues its zero
  * fill on `stream` ahead of the scan.

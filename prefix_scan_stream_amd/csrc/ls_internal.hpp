@@ -35,7 +35,7 @@ int64_t scan_sum_u32_tiles(int64_t n);
 hipError_t launch_scan_sum_u32_excl(const uint32_t* in, uint32_t* out, int64_t n, void* ws, hipStream_t stream);
 
 // ---- the scan's fixed per-device workspace (ls_noalloc.hip)
-constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(4) << 20;
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(8) << 20;
 // Device address of the current device's scratch array (NOALLOC_SCRATCH_BYTES);
 // the first call on a device enqueues its zero fill on `stream`.
 hipError_t noalloc_scratch(hipStream_t stream, void** ptr);

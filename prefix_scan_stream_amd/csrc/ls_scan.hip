@@ -55,14 +55,16 @@ constexpr int SP_CHUNKS = 13;
 constexpr int SP_TILE = SP_BLOCK * SP_CHUNKS * 4;          // 26624 elements
 constexpr int SP_FIXED_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements (deterministic)
 
-// How the single pass obtains tile prefixes for Op: chased (ls_device.hpp) or, for
-// the affine maps, by each tile walking back over 8 status words per poll.  The
-// affine maps need about 150 VGPRs, which leaves one block per CU; with 256 tiles
-// in flight they keep the walk and 32768-element tiles.
-template <class Op> constexpr bool sp_chase = true;
-template <> constexpr bool sp_chase<AffU32> = false;
-template <class Op> constexpr int sp_chunks = sp_chase<Op> ? SP_CHUNKS : SCAN_CHUNKS;
-constexpr int SP_LB_WIDE = 8;  // status words per poll of a walking tile
+// Runs per thread of the single pass, by operator.  The affine maps' combine costs
+// more registers: at 13 runs the kernel needs 151 VGPRs (one block per CU), at 8
+// runs 106 (two).  MI355X, inclusive affine scan of 2^26: 99-100 us with 8 runs
+// against 110-113 us for 32768-element tiles walking back over 8 status words per
+// poll (one block per CU), and 115 us for 13 runs with chased prefixes.
+template <class Op> constexpr int sp_chunks = SP_CHUNKS;
+template <> constexpr int sp_chunks<AffU32> = 8;
+// The workspace holds a status slot for every tile of the smallest single-pass
+// tile (run_scan checks this at compile time).
+constexpr int SP_MIN_TILE = SP_BLOCK * 8 * 4;  // 16384 elements
 
 // Tile-local part of the scan, shared by every tile a block processes: serial
 // scan of each run, wave scan of the run totals (exclusive result in wex), and
@@ -129,9 +131,9 @@ __device__ typename Op::T tile_total_by_wave(const typename Op::T* in, int64_t j
     return read_lane(wave_inclusive_scan<Op>(v), 63);
 }
 
-// One tile per block.  The chased scans (BY_INDEX) take tile = block index; the
-// others take tile ids in the order blocks start (tickets).
-// FIXED: the look-back combines a fixed set of words in a fixed order
+// One tile per block.  The chased scans (BY_INDEX: every scan but the fixed-order
+// one) take tile = block index.  FIXED takes tile ids in the order blocks start
+// (tickets), and its look-back combines a fixed set of words in a fixed order
 // (lookback_grouped), so float results are the same bits on every run.
 template <class Op, bool INCLUSIVE, bool VEC, int CHUNKS, bool FIXED = false>
 __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
 {
     using T = typename Op::T;
     using Codec = ScanCodec<Op>;
-    constexpr bool BY_INDEX = !FIXED && sp_chase<Op>;
+    constexpr bool BY_INDEX = !FIXED;
     constexpr int PARTS = CHUNKS * SP_WAVES;  // (run, wave) partial totals per tile
     constexpr int PPL = (PARTS + 63) / 64;    // partial totals per lane in their scan
     constexpr int TILE = SP_BLOCK * CHUNKS * 4;
@@ -251,16 +253,6 @@ __global__ __launch_bounds__(SP_BLOCK) void scan_single_pass_kernel(
                 if (lane == 0)
                     start_next_epoch(hdr, ep);
             }
-        } else if (tile == 0) {
-            if (lane == 0)
-                status_store(status, Codec::pack(ST_PREFIX, agg, ep));
-        } else {
-            // tickets, walking look-back (the affine maps)
-            if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_AGGREGATE, agg, ep));
-            p = lookback<Codec, SP_LB_WIDE>(status, tile, ep, hdr);
-            if (lane == 0)
-                status_store(status_word(status, tile), Codec::pack(ST_PREFIX, Op::apply(p, agg), ep));
         }
         T e = Op::apply(p, exc);
 #pragma unroll
@@ -522,7 +514,7 @@ static int64_t num_tiles_for(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE
 
 static int64_t single_pass_tiles(int64_t n, bool fixed)
 {
-    const int64_t t = fixed ? SP_FIXED_TILE : SP_TILE;  // the smallest tile of each scheme
+    const int64_t t = fixed ? SP_FIXED_TILE : SP_MIN_TILE;  // the smallest tile of each scheme
     return (n + t - 1) / t;
 }
 
@@ -626,6 +618,8 @@ static hipError_t run_scan(const void* in, void* out, int64_t n, bool inclusive,
     }
     constexpr int CHUNKS = FIXED ? SCAN_CHUNKS : sp_chunks<Op>;
     constexpr int64_t TILE = int64_t(SP_BLOCK) * CHUNKS * 4;
+    static_assert(TILE >= (FIXED ? SP_FIXED_TILE : SP_MIN_TILE),
+                  "a tile smaller than the workspace's would index status slots past its end");
     const int64_t tiles = (n + TILE - 1) / TILE;  // never more than the workspace holds
     auto* hdr = reinterpret_cast<WsHeader*>(ws);
     auto* status = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + sizeof(WsHeader));

@@ -166,11 +166,11 @@ def test_noalloc_scan_validation(lib):
     far = A_IN - (1 << 40)  # far enough below `in` that the large sizes do not overlap it
     assert f(A_IN, far, ps.SCAN_NOALLOC_MAX_N + 1, INT32, SUM, 1, None, None) == WS
     assert f(A_IN, far, 1 << 36, F32, MAX, 0, None, None) == WS
-    # the fixed 4 MiB workspace holds the single pass's status words at the maximum n
+    # the fixed 8 MiB workspace holds the single pass's status words at the maximum n
     for t, op in ((INT32, SUM), (F32, SUM), (UINT32, AFFINE)):
         need = ctypes.c_size_t(0)
         assert lib.ls_scan_workspace_bytes(ps.SCAN_NOALLOC_MAX_N, t, op, ctypes.byref(need)) == 0
-        assert need.value <= 4 << 20
+        assert need.value <= 8 << 20
 
 
 def test_extended_entry_points_validation(lib):
@@ -181,9 +181,10 @@ def test_extended_entry_points_validation(lib):
     single = ctypes.c_size_t(0)
     lib.ls_scan_ex_workspace_bytes(1 << 20, F32, SUM, 0, ctypes.byref(single))
     lib.ls_scan_ex_workspace_bytes(1 << 20, F32, SUM, 3, ctypes.byref(sz))
-    # a 256-byte header and one 256-byte status slot per tile: 26624-element tiles for
-    # the single pass, 32768 for the deterministic one
-    assert single.value == 256 + 256 * -(-(1 << 20) // 26624)
+    # a 256-byte header and one 256-byte status slot per tile of the smallest tile:
+    # 16384 elements for the single pass (the affine maps'), 32768 for the
+    # deterministic one
+    assert single.value == 256 + 256 * -(-(1 << 20) // 16384)
     assert sz.value == 256 + 256 * -(-(1 << 20) // 32768)
     assert lib.ls_scan_ex_workspace_bytes(1 << 20, INT32, SUM, 4, ctypes.byref(sz)) == INV
     assert lib.ls_scan_ex_workspace_bytes(10, F32, XOR, 1, ctypes.byref(sz)) == UNS

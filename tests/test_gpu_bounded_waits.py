@@ -33,7 +33,7 @@ DEV = torch.device("cuda:0")
 LIB = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "prefix_scan_stream_amd", "libscan_spin1.so")
 INT32, UINT32, F32 = 0, 1, 2
-SUM, MAX = 0, 1
+SUM, MAX, AFFINE = 0, 1, 7
 LT, DETERMINISTIC, INCOMPLETE = 0, 3, 5
 N = 1 << 25            # hundreds of tiles: the ticket paths
 N_FALLBACK = (1 << 22) + 12345  # 158 scan tiles, 129 compaction tiles: the forced fallbacks
@@ -97,16 +97,18 @@ def values(n=N, seed=901):
 # ------------------------------------------------ block-index tiles: exact fallbacks
 
 @pytest.mark.parametrize("dtype,op,inclusive", [("int32", "sum", False), ("float32", "sum", True),
-                                                ("int32", "max", True), ("float32", "max", False)])
+                                                ("int32", "max", True), ("float32", "max", False),
+                                                ("uint32", "affine", True)])
 def test_scan_fallback_replays_the_same_bits(lib, dtype, op, inclusive):
     """Every tile replays its prefix instead of waiting: the result is the oracle's
-    (integers, max) and the same bits as the normal library's (float sums)."""
+    (integers, max, affine maps: the replay combines in element order) and the same
+    bits as the normal library's (float sums)."""
     print(f"forced-fallback scan {dtype} {op} inclusive={inclusive} n={N_FALLBACK}", flush=True)
     xh = wl.case(dtype, op, N_FALLBACK, seed=930)
     x = torch.from_numpy(xh).to(DEV)
     y = torch.empty_like(x)
-    t = {"int32": INT32, "float32": F32}[dtype]
-    o = {"sum": SUM, "max": MAX}[op]
+    t = {"int32": INT32, "uint32": UINT32, "float32": F32}[dtype]
+    o = {"sum": SUM, "max": MAX, "affine": AFFINE}[op]
     ws = workspace(lib.ls_scan_workspace_bytes, N_FALLBACK, t, o)
     for rep in range(2):  # the second call runs under the next epoch of the same workspace
         y.fill_(7)
@@ -116,7 +118,7 @@ def test_scan_fallback_replays_the_same_bits(lib, dtype, op, inclusive):
         got = y.cpu().numpy()
         want = (ps.scan_inclusive if inclusive else ps.scan_exclusive)(x, op).cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"call {rep}"
-        if dtype == "int32":
+        if dtype != "float32":
             assert np.array_equal(got, oracle.scan(xh, op, inclusive).y)
 
 
