@@ -9,6 +9,8 @@ include/libscan.h are exported.
 build_bounded_wait_test_lib() builds the same sources into libscan_spin1.so with
 every bounded wait (look-back, chased prefixes) giving up after one empty poll.
 Only the test of the workspace error word loads it; the package never does.
+build_tiny_tile_lib() builds them into libscan_tiny.so with 256-element scan tiles,
+for the tests that follow the pages' block decomposition tile by tile.
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ BUILD = os.path.join(PKG, "_build")
 HEADER = os.path.join(ROOT, "include", "libscan.h")
 LIB = os.path.join(PKG, "libscan.so")
 SPIN1_LIB = os.path.join(PKG, "libscan_spin1.so")
+TINY_LIB = os.path.join(PKG, "libscan_tiny.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -98,6 +101,13 @@ def build_ceiling_lib(verbose: bool = False) -> str:
     if verbose:
         print(f"built {CEILING_LIB}")
     return CEILING_LIB
+
+
+def build_tiny_tile_lib(verbose: bool = False) -> str:
+    """libscan_tiny.so: the scans with 256-element tiles (one wave, one run of four
+    per thread), so that a handful of elements spans several tiles (test use only)."""
+    return build(verbose, TINY_LIB, os.path.join(BUILD, "tiny"),
+                 ("-DLS_SCAN_BLOCK=64", "-DLS_SCAN_CHUNKS=1", "-DLS_SP_BLOCK=64", "-DLS_SP_CHUNKS=1"))
 
 
 def build_bounded_wait_test_lib(verbose: bool = False) -> str:

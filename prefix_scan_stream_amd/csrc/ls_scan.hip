@@ -51,7 +51,10 @@ static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanne
 #endif
 constexpr int SP_BLOCK = LS_SP_BLOCK;
 constexpr int SP_WAVES = SP_BLOCK / 64;
-constexpr int SP_CHUNKS = 13;
+#ifndef LS_SP_CHUNKS
+#define LS_SP_CHUNKS 13
+#endif
+constexpr int SP_CHUNKS = LS_SP_CHUNKS;
 constexpr int SP_TILE = SP_BLOCK * SP_CHUNKS * 4;          // 26624 elements
 constexpr int SP_FIXED_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements (deterministic)
 
@@ -60,11 +63,12 @@ constexpr int SP_FIXED_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements (de
 // runs 106 (two).  MI355X, inclusive affine scan of 2^26: 99-100 us with 8 runs
 // against 110-113 us for 32768-element tiles walking back over 8 status words per
 // poll (one block per CU), and 115 us for 13 runs with chased prefixes.
+constexpr int SP_AFF_CHUNKS = SP_CHUNKS < 8 ? SP_CHUNKS : 8;
 template <class Op> constexpr int sp_chunks = SP_CHUNKS;
-template <> constexpr int sp_chunks<AffU32> = 8;
+template <> constexpr int sp_chunks<AffU32> = SP_AFF_CHUNKS;
 // The workspace holds a status slot for every tile of the smallest single-pass
 // tile (run_scan checks this at compile time).
-constexpr int SP_MIN_TILE = SP_BLOCK * 8 * 4;  // 16384 elements
+constexpr int SP_MIN_TILE = SP_BLOCK * SP_AFF_CHUNKS * 4;  // 16384 elements
 
 // Tile-local part of the scan, shared by every tile a block processes: serial
 // scan of each run, wave scan of the run totals (exclusive result in wex), and
