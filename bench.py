@@ -331,7 +331,7 @@ def main():
             ms = timer.run(lambda i, sc=scheme: ps.scan_ex(x, "sum", False, sc, out=out), K, W)
             gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
             result_legs[f"scheme_{scheme}_i32_excl_2e28"] = {
-                "us": round(ms * 1e3, 1), "gelem_s": round(n / ms / 1e6, 1),
+                "us": round(ms * 1e3, 1), **timer.spread(), "gelem_s": round(n / ms / 1e6, 1),
                 "algo_gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                 "bytes_moved_per_elem": 4 * moved}
             log(f"scheme {scheme}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s (algorithmic)")
