@@ -5,7 +5,7 @@
 // scatter (geek-doc.cn parallel prefix scan page, section 一; pgsm.cn SIMT page,
 // section 4.2, which also writes the count on the device).  Here the three steps
 // are fused per tile and the flags and indices never leave the chip:
-//   1. a tile (32768 elements) is loaded with 128-bit loads into registers;
+//   1. a tile (16384 elements) is loaded with 128-bit loads into registers;
 //   2. the predicate is evaluated in registers; kept elements are counted per run
 //      of 4 and the counts scanned (DPP wave scan, then one wave over the
 //      (run, wave) counts); the tile's total is published at once;
@@ -17,8 +17,8 @@
 //      lanes on consecutive addresses; the last tile writes the count.
 // Blocks are persistent and pipelined: the next tile's loads and count run while
 // the current tile's look-back does.  No atomics touch the data; the only
-// atomics are the tile-id counter and the status words.  HBM traffic: n*4 bytes
-// read, count*4 bytes written.
+// atomics are the status words and the count of started blocks.  HBM traffic:
+// n*4 bytes read, count*4 bytes written.
 #include "ls_device.hpp"
 #include "ls_internal.hpp"
 
@@ -69,7 +69,8 @@ enum CompactSrc : int { SRC_CMP = 0, SRC_FLAGS = 1 };    // (x CMP thr) / flag b
 enum CompactPay : int { PAY_VALUE = 0, PAY_INDEX = 1 };  // x itself / its index (uint32)
 
 // The staging buffer is dynamic LDS so that the compiler's occupancy model does
-// not cap the register budget by it (one block per CU either way).
+// not cap the register budget by it: with the buffer static the compiler aimed at
+// one block per CU and used up to 168 VGPRs; dynamic, it fits two (at most 128).
 #ifdef LS_CP_WPE
 #define LS_CP_WAVES_ATTR __attribute__((amdgpu_waves_per_eu(LS_CP_WPE)))
 #else
@@ -77,23 +78,24 @@ enum CompactPay : int { PAY_VALUE = 0, PAY_INDEX = 1 };  // x itself / its index
 #endif
 
 // Persistent blocks of CP_WAVES data waves and one control wave; a tile is
-// 32768 elements, staged whole in 128 KiB of LDS, one block per CU.  Tiles of a
-// block are numbered k = 0, 1, ... in the order it handles them; at the top of
-// step k, tile k is counted (its tile-local offsets and total are in LDS) and
-// the id of tile k+1 is known.
+// 16384 elements, staged whole in 64 KiB of LDS, two blocks per CU.  Block b of
+// G handles tiles b, b + G, b + 2G, ... (tile ids by block index: no counter);
+// its tiles are numbered k = 0, 1, ... in that order.  At the top of step k, tile
+// k is counted (its tile-local offsets and total are in LDS).
 //   data waves: stage tile k's kept elements at their ranks, run by run, each
 //     run's registers then taking tile k+1's run, so its loads start with the
 //     staging; count tile k+1 -- the last data wave to finish scans the
-//     (run, wave) counts and publishes the tile's total at once; take the id of
-//     tile k+2 meanwhile (one step ahead, so the counter's latency is hidden).
+//     (run, wave) counts and publishes the tile's total at once.
 //   control wave, meanwhile: tile k's output offset by look-back; publish the
 //     full prefix.
 //   [barrier]  data waves: copy tile k out.  [barrier]
-// The look-back and the copy run while tile k+1 loads.  Tiles of 32768
-// elements halve the tile-id atomics against 16384: one device-scope atomic on
-// one address serializes at about 15 ns, which caps a persistent read of 64 KiB
-// tiles at about 4.3 TB/s on MI355X (6.7 TB/s with the same tiles assigned
-// statically).
+// The look-back and the copy run while tile k+1 loads.  A look-back that waits
+// longer than the fallback time counts the missing tiles itself, so a block that
+// is not yet resident costs time, never a wrong result; the grid is capped at the
+// blocks that are resident at once all the same (resident_blocks below).
+// 16384-element tiles, two blocks per CU, measured 113 / 137 / 178 us on MI355X
+// (2^27 int32, 1 / 50 / 99 % kept) against 109 / 145 / 191 us for 32768-element
+// tiles, one block per CU.
 template <int DT, bool VEC, int SRC = SRC_CMP, int PAY = PAY_VALUE, bool FLAG4 = true>
 LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(const uint32_t* __restrict__ in,
                                                              uint32_t* __restrict__ out, int64_t n,
