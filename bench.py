@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -46,11 +47,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments or blank lines, each line stripped: what the
+    compiler sees, so that a change to a comment keeps the recorded counters."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).strip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

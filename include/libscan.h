@@ -50,10 +50,16 @@
  *   - The radix sort and the three-phase scan_ex schemes use their workspace as
  *     plain scratch: its contents on entry do not matter.  (For the sort's error
  *     word to be meaningful, initialise its workspace once.)
- *   Each wait for another tile is bounded: after about one second without
- *   progress it gives up, the call's output is then incomplete, and the
- *   workspace records the fact; ls_workspace_check reports it.  In a correct run
- *   no wait lasts more than microseconds.
+ *   Each wait for another tile is bounded in time.  The single-pass scans
+ *   (except the deterministic scheme) and the compactions take tiles by block
+ *   index: a tile that has waited about a millisecond computes what it waited
+ *   for from the input itself, and the result stays exact.  The deterministic
+ *   scan and the segmented scans take tile ids in the order blocks start: a
+ *   wait there gives up after about one second, the call's output is then
+ *   incomplete, and the workspace records the fact; so does a call whose last
+ *   tile waits more than about ten seconds for the other blocks to start.
+ *   ls_workspace_check reports it.  In a correct run no wait lasts more than
+ *   microseconds.
  */
 #ifndef LIBSCAN_H
 #define LIBSCAN_H

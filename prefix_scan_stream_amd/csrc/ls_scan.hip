@@ -36,16 +36,17 @@ constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_CHUNKS * 4;  // 16384 elements (thre
 
 static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanned by one wave");
 
-// The single pass uses 8-wave blocks.  Each tile takes one device-scope atomic on
-// the tile counter (they serialize at about 15 ns), and a tile holds its data in
-// registers until its prefix is known, so the tile size sets both the counter's
-// share of the time and how long the pipeline of resident tiles takes to fill
-// and drain (two blocks per CU: 512 tiles).  With chased prefixes, 13 runs per
-// thread (26624-element tiles) measured best: 2^28 in 338-340 us, against
-// 341-343 for 12 and 14 runs, 345-348 for 16 (32768) and 351 for 8 (16384).  The
-// deterministic scheme keeps 16 runs: its fixed groups of 64 tiles are slower
-// with smaller tiles (float32 2^26: 98 against 100-102 us).  16-wave blocks with
-// 65536-element tiles (one block per CU) were slower (373-381 us).
+// The single pass uses 8-wave blocks.  A tile holds its data in registers until
+// its prefix is known, so the tile size sets how long the pipeline of resident
+// tiles takes to fill and drain (two blocks per CU: 512 tiles), against the
+// number of tiles the chasing wave must cover.  13 runs per thread (26624-element
+// tiles) measured best: 2^28 in 338-340 us, against 341-343 for 12 and 14 runs,
+// 345-348 for 16 (32768) and 351 for 8 (16384) (measured while tiles still took
+// their ids from a counter atomic; tiles by block index then took 13 runs from
+// 334 to 326 us).  The deterministic scheme keeps 16 runs: its fixed groups of 64
+// tiles are slower with smaller tiles (float32 2^26: 98 against 100-102 us).
+// 16-wave blocks with 65536-element tiles (one block per CU) were slower
+// (373-381 us).
 #ifndef LS_SP_BLOCK
 #define LS_SP_BLOCK 512
 #endif
