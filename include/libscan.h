@@ -46,7 +46,10 @@
  *     calls its contents must not change, and it must serve no other purpose: a
  *     status workspace used by a radix sort or a three-phase scan_ex, or written
  *     in any other way, must be initialised again.  Apart from that it may serve
- *     any sequence of these calls, of any sizes it is large enough for.
+ *     any sequence of these calls, of any sizes it is large enough for, up to
+ *     2^26 calls: the words carry the call's epoch, compared modulo 2^26, so
+ *     initialise it again before that many calls (the Python binding does so
+ *     every 2^25).
  *   - The radix sort and the three-phase scan_ex schemes use their workspace as
  *     plain scratch: its contents on entry do not matter.  (For the sort's error
  *     word to be meaningful, initialise its workspace once.)

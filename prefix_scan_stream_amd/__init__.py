@@ -172,6 +172,8 @@ def ls_compact_workspace_bytes(n: int, dtype: str) -> int:
 # ------------------------------------------------------------ workspaces
 
 _ws_cache: dict = {}    # (device index, stream handle) -> the uint8 workspace in use
+_ws_uses: dict = {}     # calls on each cached status workspace since its last initialisation
+STATUS_REINIT_CALLS = 1 << 25
 _ws_retired: list = []  # workspaces replaced by larger ones, kept for graphs that captured them
 
 
@@ -219,7 +221,15 @@ def workspace_for(device: torch.device, stream: torch.cuda.Stream, nbytes: int,
         if buf is not None:
             _ws_retired.append(buf)
         _ws_cache[key] = new
+        _ws_uses[key] = 0
         buf = new
+    elif kind == "status":
+        # status words compare epochs modulo 2^26: zero the workspace again well
+        # before that many calls (one fill kernel per 2^25 calls)
+        _ws_uses[key] = _ws_uses.get(key, 0) + 1
+        if _ws_uses[key] >= STATUS_REINIT_CALLS:
+            ls_workspace_init(buf, stream)
+            _ws_uses[key] = 0
     return buf
 
 
@@ -237,6 +247,7 @@ def release_workspaces() -> None:
     replayed afterwards)."""
     _ws_cache.clear()
     _ws_retired.clear()
+    _ws_uses.clear()
 
 
 def _after_call(ws: torch.Tensor, stream, where: str) -> None:

@@ -516,18 +516,29 @@ struct ScanCodec {
 
 // Compaction counts: a 36-bit count (n < 2^36 elements).  Tile totals are at
 // most one tile's elements; only full prefixes are large.
+// Word layout: flag 63..62, the count's bits 35..32 in 61..58, the epoch's low 26
+// bits in 57..32, the count's bits 31..0 in 31..0.  Every codec keeps its epoch's
+// low bits from bit 32 up, so that one workspace can serve scans, segmented scans
+// and compactions in turn: a word that another codec wrote in an earlier call
+// reads as empty unless the two epochs differ by a multiple of 2^26 (the count
+// codec's epoch width).  (With the epoch above the whole 36-bit count, a count
+// word written at epoch e read as epoch 16 e to the scan codec.)
 struct CountCodec {
     using V = uint64_t;
     static constexpr uint64_t MASK = (uint64_t(1) << 36) - 1;
     static constexpr uint32_t EPOCH_MASK = (1u << 26) - 1u;
     static __device__ __forceinline__ uint32_t flag(uint64_t w, uint32_t ep)
     {
-        return ((uint32_t(w >> 36) & EPOCH_MASK) == (ep & EPOCH_MASK)) ? uint32_t(w >> 62) : ST_EMPTY;
+        return ((uint32_t(w >> 32) & EPOCH_MASK) == (ep & EPOCH_MASK)) ? uint32_t(w >> 62) : ST_EMPTY;
     }
-    static __device__ __forceinline__ V value(uint64_t w) { return w & MASK; }
+    static __device__ __forceinline__ V value(uint64_t w)
+    {
+        return (((w >> 58) & 0xfull) << 32) | (w & 0xffffffffull);
+    }
     static __device__ __forceinline__ uint64_t pack(uint32_t f, V v, uint32_t ep)
     {
-        return (uint64_t(f) << 62) | (uint64_t(ep & EPOCH_MASK) << 36) | (v & MASK);
+        return (uint64_t(f) << 62) | (((v >> 32) & 0xfull) << 58) | (uint64_t(ep & EPOCH_MASK) << 32) |
+               (v & 0xffffffffull);
     }
     static __device__ __forceinline__ V identity() { return 0; }
     static __device__ __forceinline__ V apply(V a, V b) { return a + b; }
