@@ -260,7 +260,8 @@ ls_status scan_ex(const void *in, void *out, int64_t n, ls_dtype t, ls_op op, in
  * fixed 8 MiB array in device memory per GPU (held until the process ends) and
  * uses it as the single-pass scan's workspace; the call itself allocates and frees
  * nothing.  The first call on a device looks the array up and enqueues its zero
- * fill on `stream` ahead of the scan.
+ * fill on `stream` ahead of the scan; every 2^25-th call after that enqueues the
+ * fill again (the array's status words compare epochs modulo 2^26).
  *   exclusive  nonzero: exclusive scan; zero: inclusive.
  *   n          0 <= n <= LS_SCAN_NOALLOC_MAX_N; a larger n returns
  *              LS_ERR_WORKSPACE and enqueues nothing.

@@ -19,8 +19,12 @@ static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 namespace {
 
 constexpr int NOALLOC_MAX_DEVICES = 64;
+// Status words compare epochs modulo 2^26 at the least: the array is zeroed again
+// after this many calls on a device (one fill kernel ahead of the call's scan).
+constexpr int64_t NOALLOC_REINIT_CALLS = int64_t(1) << 25;
 std::mutex g_scratch_mu;
-void* g_scratch_ptr[NOALLOC_MAX_DEVICES];  // device address of `scratch` on each device, once known
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];     // device address of `scratch` on each device, once known
+int64_t g_scratch_calls[NOALLOC_MAX_DEVICES];  // calls since the last zero fill
 
 }  // namespace
 
@@ -32,9 +36,16 @@ __global__ __launch_bounds__(256) void scratch_zero_kernel(u32x4* p, int64_t wor
         p[i] = z;
 }
 
+static hipError_t zero_scratch(void* p, hipStream_t s)
+{
+    constexpr int64_t words = int64_t(NOALLOC_SCRATCH_BYTES / 16);
+    hipLaunchKernelGGL(scratch_zero_kernel, dim3(256), dim3(256), 0, s, reinterpret_cast<u32x4*>(p), words);
+    return hipGetLastError();
+}
+
 // Device address of this device's scratch array.  The first call on a device
 // looks it up and enqueues a zero fill of the whole array on `s`, ahead of the
-// caller's work on the same stream.
+// caller's work on the same stream; so does every NOALLOC_REINIT_CALLS-th call.
 hipError_t noalloc_scratch(hipStream_t s, void** ptr)
 {
     int dev = -1;
@@ -51,12 +62,14 @@ hipError_t noalloc_scratch(hipStream_t s, void** ptr)
             return e;
         if (p == nullptr)
             return hipErrorInvalidSymbol;
-        constexpr int64_t words = int64_t(NOALLOC_SCRATCH_BYTES / 16);
-        hipLaunchKernelGGL(scratch_zero_kernel, dim3(256), dim3(256), 0, s, reinterpret_cast<u32x4*>(p), words);
-        e = hipGetLastError();
-        if (e != hipSuccess)
+        if ((e = zero_scratch(p, s)) != hipSuccess)
             return e;
         g_scratch_ptr[dev] = p;
+        g_scratch_calls[dev] = 0;
+    } else if (++g_scratch_calls[dev] >= NOALLOC_REINIT_CALLS) {
+        if ((e = zero_scratch(g_scratch_ptr[dev], s)) != hipSuccess)
+            return e;
+        g_scratch_calls[dev] = 0;
     }
     *ptr = g_scratch_ptr[dev];
     return hipSuccess;
