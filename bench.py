@@ -162,7 +162,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--legs", default=",".join(DEFAULT_LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
