@@ -17,7 +17,7 @@ library launches on give the time.  The JSON line also carries:
                 copy kernels of libls_ceiling.so over the headline's bytes (the
                 practical bandwidth ceilings).  Each leg reports its mean, median and
                 minimum time per call.
-Only rank 0 of one GPU exists here; --gpus above 1 is refused.
+The benchmark runs on one GPU (rank 0); --gpus above 1 is refused.
 """
 from __future__ import annotations
 
@@ -167,7 +167,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported",
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr)
         sys.exit(2)
     legs = [s for s in args.legs.split(",") if s]

@@ -2,8 +2,8 @@
 
 Every kernel must keep its tile in registers: no private (scratch) segment and no
 register spills -- a run-time index into a register array silently moves the tile
-to per-lane scratch memory.  Packed fp32 VALU forms must not appear (the build
-disables them)."""
+to per-lane scratch memory.  Packed fp32 VALU forms must not appear (the compile
+flags disable them)."""
 import os
 import re
 import subprocess
