@@ -337,8 +337,11 @@ __device__ __forceinline__ void store_run(T* __restrict__ p, int64_t idx, int64_
 // whose epoch is not the reader's reads as empty, so words left by earlier calls
 // never need clearing.
 //   32-bit payload (scans): bits 63..62 flag, 61..32 epoch (30 bits), 31..0 value.
-//   36-bit payload (compaction counts): 63..62 flag, 61..36 epoch (26 bits),
-//     35..0 count.
+//   36-bit payload (compaction counts): 63..62 flag, 61..58 count bits 35..32,
+//     57..32 epoch (26 bits), 31..0 count bits 31..0.
+// The segmented scan's words add a head bit (ls_segmented.hip).  Every format keeps
+// its epoch's low bits from bit 32 up, so a word of one format never reads as
+// current to a reader of another at a later epoch.
 // Each tile's word sits alone in a 256-byte slot.  Packed eight to a cache line,
 // the words of neighbouring tiles are published and polled by hundreds of waves
 // at once through one line; measured on MI355X that contention slowed the whole
