@@ -15,8 +15,11 @@ library launches on give the time.  The JSON line also carries:
                 float32 sum and int32 max scans (N = 2^26), the two batched row
                 shapes, the 2^20 scan (latency-bound), and the plain read / write /
                 copy kernels of libls_ceiling.so over the headline's bytes (the
-                practical bandwidth ceilings).  Each leg reports its mean, median and
-                minimum time per call.
+                practical bandwidth ceilings).  A leg runs W warmup calls, then
+                more untimed calls until the GPU has been busy for 50 ms (the host
+                prepares each workload while the GPU idles), then six timed batches
+                of K calls; it reports the first batch's mean and the median and
+                minimum of the batch means, per call.
 The benchmark runs on one GPU (rank 0); --gpus above 1 is refused.
 """
 from __future__ import annotations
@@ -36,6 +39,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Each bandwidth leg keeps calling its workload, untimed, until the GPU has been busy
+# this long after the warmup calls, before the timed batches start.
+LEG_SETTLE_MS = 50.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_i32_excl_n2e28_hbm_counters.txt")
 SCAN_SOURCES = ["prefix_scan_stream_amd/csrc/ls_scan.hip", "prefix_scan_stream_amd/csrc/ls_device.hpp"]
 ALL_LEGS = ("scan", "small", "fp32", "max", "compact", "rows64", "rows1024", "ceiling", "schemes",
@@ -107,9 +113,21 @@ class Timer:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    def run(self, fn, steps: int, warmup: int) -> float:
+    def run(self, fn, steps: int, warmup: int, settle_ms: float = 0.0) -> float:
         for i in range(warmup):
             fn(i)
+        if settle_ms > 0:
+            # more untimed calls until the GPU has been busy for settle_ms: after
+            # the host-side preparation of a workload the GPU has idled for a while
+            torch = self.torch
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            i = warmup
+            while (time.perf_counter() - t0) * 1e3 < settle_ms:
+                for _ in range(8):
+                    fn(i)
+                    i += 1
+                torch.cuda.synchronize()
         ms = self._batch(fn, steps)
         self.batches = [ms] + [self._batch(fn, steps) for _ in range(self.REPEATS)]
         return ms  # ms per step of the first batch
@@ -245,7 +263,7 @@ def main():
 
     def bw_leg(name, xs, fn, elems, nbytes):
         outs = [torch.empty_like(t) for t in xs]
-        ms = timer.run(lambda i: fn(xs[i % len(xs)], outs[i % len(outs)]), K, W)
+        ms = timer.run(lambda i: fn(xs[i % len(xs)], outs[i % len(outs)]), K, W, settle_ms=LEG_SETTLE_MS)
         gbs = nbytes / (ms * 1e-3) / 1e9
         result_legs[name] = {"us": round(ms * 1e3, 1), **timer.spread(),
                              "gelem_s": round(elems / ms / 1e6, 1), "algo_gbs": round(gbs, 1),

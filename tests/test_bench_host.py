@@ -63,3 +63,65 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+class _FakeCuda:
+    """Stands in for torch.cuda: events read a clock that every call advances."""
+
+    def __init__(self):
+        self.now_ms = 0.0
+        self.syncs = 0
+
+    def synchronize(self):
+        self.syncs += 1
+
+    def Event(self, enable_timing=True):
+        cuda = self
+
+        class _Ev:
+            def record(self):
+                self.t = cuda.now_ms
+
+            def elapsed_time(self, other):
+                return other.t - self.t
+
+        return _Ev()
+
+
+class _FakeTorch:
+    def __init__(self):
+        self.cuda = _FakeCuda()
+
+
+def test_legs_settle_before_the_timed_batches():
+    """After the warmup calls a leg keeps calling, untimed, until the GPU has been busy
+    for settle_ms; the timed batches then hold exactly `steps` calls each."""
+    torch = _FakeTorch()
+    calls = []
+
+    def fn(i):
+        calls.append(i)
+        torch.cuda.now_ms += 0.1  # the call's GPU time
+        bench.time.sleep(0.0005)
+
+    t = bench.Timer(torch)
+    ms = t.run(fn, steps=4, warmup=3, settle_ms=20.0)
+    timed = 4 * (1 + bench.Timer.REPEATS)
+    untimed = len(calls) - timed
+    assert untimed > 3 + 8  # the warmup calls, then at least one round of settle calls
+    assert (untimed - 3) % 8 == 0
+    assert calls == list(range(untimed)) + list(range(4)) * (1 + bench.Timer.REPEATS)
+    assert abs(ms - 0.1) < 1e-9
+    assert len(t.batches) == 1 + bench.Timer.REPEATS
+
+
+def test_headline_timing_takes_exactly_the_warmup_calls():
+    torch = _FakeTorch()
+    calls = []
+
+    def fn(i):
+        calls.append(i)
+        torch.cuda.now_ms += 0.2
+
+    bench.Timer(torch).run(fn, steps=5, warmup=7)
+    assert len(calls) == 7 + 5 * (1 + bench.Timer.REPEATS)
