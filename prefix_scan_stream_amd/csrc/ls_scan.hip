@@ -7,14 +7,16 @@
 // totals to one another inside one launch through flags in global memory.  That
 // is the design used here, because only it moves the minimum 2*n*4 bytes that
 // bound an HBM-limited scan:
-//   1. a block takes the next tile id (start order, so it only ever waits for
-//      blocks already running) and loads its 26624-element tile with 128-bit
-//      loads;
+//   1. a block's tile is its block index (the fixed-order scheme instead takes
+//      the next tile id from a counter, in the order blocks start); it loads the
+//      tile (26624 elements; 16384 for the affine maps) with 128-bit loads;
 //   2. it scans the tile in registers (serial runs of 4, DPP wave scan, one wave
 //      over the (run, wave) totals) and publishes the tile total;
 //   3. its first wave waits for the full prefix of the previous tile, which one
 //      chasing wave publishes for every tile in order from the published totals
-//      (the wave that scanned tile 0 stays on for this; see ls_device.hpp);
+//      (the wave that scanned tile 0 stays on for this; see ls_device.hpp); a
+//      tile that has waited a millisecond computes that prefix itself, since
+//      the blocks it waits for may not have started;
 //   4. it writes prefix (+) local scan with 128-bit stores.
 // Each tile status is one 64-bit word (flag + value) so a single atomic access
 // carries both; see ls_device.hpp.
