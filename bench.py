@@ -1,6 +1,6 @@
 """Benchmark of libscan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs scan,compact,...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs scan,compact,...] [--settle-ms S]
 
 A step is one device-wide int32 exclusive sum scan of N = 2^28 elements (values
 U{0..15}), inputs resident in HBM.  The headline `value` is Gelem/s over exactly K
@@ -16,8 +16,8 @@ library launches on give the time.  The JSON line also carries:
                 shapes, the 2^20 scan (latency-bound), and the plain read / write /
                 copy kernels of libls_ceiling.so over the headline's bytes (the
                 practical bandwidth ceilings).  A leg runs W warmup calls, then
-                more untimed calls until the GPU has been busy for 50 ms (the host
-                prepares each workload while the GPU idles), then six timed batches
+                more untimed calls until the GPU has been busy for S ms (default 50;
+                the host prepares each workload while the GPU idles), then six timed batches
                 of K calls; it reports the first batch's mean and the median and
                 minimum of the batch means, per call.
 The benchmark runs on one GPU (rank 0); --gpus above 1 is refused.
@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--legs", default=",".join(DEFAULT_LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=LEG_SETTLE_MS,
+                    help="untimed GPU-busy time of each leg after its warmup (0: none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported",
@@ -263,7 +265,7 @@ def main():
 
     def bw_leg(name, xs, fn, elems, nbytes):
         outs = [torch.empty_like(t) for t in xs]
-        ms = timer.run(lambda i: fn(xs[i % len(xs)], outs[i % len(outs)]), K, W, settle_ms=LEG_SETTLE_MS)
+        ms = timer.run(lambda i: fn(xs[i % len(xs)], outs[i % len(outs)]), K, W, settle_ms=args.settle_ms)
         gbs = nbytes / (ms * 1e-3) / 1e9
         result_legs[name] = {"us": round(ms * 1e3, 1), **timer.spread(),
                              "gelem_s": round(elems / ms / 1e6, 1), "algo_gbs": round(gbs, 1),
@@ -355,7 +357,8 @@ def main():
         x = to_dev(wl.big_scan())
         out = torch.empty_like(x)
         for scheme, moved in (("reduce_then_scan", 3), ("scan_then_propagate", 4)):
-            ms = timer.run(lambda i, sc=scheme: ps.scan_ex(x, "sum", False, sc, out=out), K, W)
+            ms = timer.run(lambda i, sc=scheme: ps.scan_ex(x, "sum", False, sc, out=out), K, W,
+                           settle_ms=args.settle_ms)
             gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
             result_legs[f"scheme_{scheme}_i32_excl_2e28"] = {
                 "us": round(ms * 1e3, 1), **timer.spread(), "gelem_s": round(n / ms / 1e6, 1),
@@ -380,7 +383,8 @@ def main():
         ok_, ov_ = torch.empty_like(keys), torch.empty_like(vals)
         for name, v, per_pass in (("sort_u32_pairs_2e24", vals, 20), ("sort_u32_keys_2e24", None, 12)):
             ms = timer.run(lambda i, v=v: ps.radix_sort(keys, v, out_keys=ok_,
-                                                        out_values=ov_ if v is not None else None), K, W)
+                                                        out_values=ov_ if v is not None else None), K, W,
+                           settle_ms=args.settle_ms)
             moved = 4 * per_pass * n
             result_legs[name] = {"us": round(ms * 1e3, 1), **timer.spread(), "gkeys_s": round(n / ms / 1e6, 2),
                                  "moved_gbs": round(moved / (ms * 1e-3) / 1e9, 1),
@@ -398,7 +402,8 @@ def main():
         for kind, nbytes in (("read", 4 * n), ("write", 4 * n), ("copy", 8 * n)):
             best = None
             for bpc in (4, 8, 16):
-                ms = timer.run(lambda i, k=kind, bpc=bpc: ce.call(k, torch, a, b, sink, bpc), K, W)
+                ms = timer.run(lambda i, k=kind, bpc=bpc: ce.call(k, torch, a, b, sink, bpc), K, W,
+                               settle_ms=args.settle_ms)
                 if best is None or ms < best[0]:
                     best = (ms, bpc, timer.spread())
             ms, bpc, spread = best
