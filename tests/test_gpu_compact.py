@@ -11,7 +11,7 @@ from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 
 pytestmark = pytest.mark.gpu
 
-TILE = 32768  # the library's compaction tile; sizes below also cover half and quarter tiles
+TILE = 16384  # the library's compaction tile; sizes below also cover half and quarter tiles
 SENTINEL = 0xDEADBEEF
 
 
@@ -33,8 +33,9 @@ def check_compact(x: np.ndarray, cmp: str, thr, *, offset=0):
     assert np.all(bits(got[c:]) == SENTINEL), "wrote beyond the count"
 
 
-@pytest.mark.parametrize("n", [1, 2, 17, 64, 4095, 4096, 4097, 8191, 16385, TILE - 1, TILE, TILE + 1,
-                               3 * TILE + 5, 70 * TILE + 9, 200_003, 300 * TILE + 11])
+@pytest.mark.parametrize("n", [1, 2, 17, 64, 4095, 4096, 4097, 8191, TILE - 1, TILE, TILE + 1, 2 * TILE - 1,
+                               2 * TILE + 1, 3 * TILE + 5, 70 * TILE + 9, 200_003, 300 * TILE + 11,
+                               1100 * TILE + 7])
 @pytest.mark.parametrize("dtype", ["int32", "uint32", "float32"])
 @pytest.mark.parametrize("cmp", ["lt", "le", "gt", "ge", "eq", "ne"])
 def test_compact_matches_oracle(dtype, cmp, n):
@@ -59,6 +60,21 @@ def test_compact_selectivities(sel):
     thr = (1 << 31) - 1 if sel == 1.0 else wl.threshold_for(sel)
     cmp = "le" if sel == 1.0 else "lt"
     check_compact(x, cmp, np.int32(thr))
+
+
+def test_compact_mixed_density_tiles():
+    """One call over regions that keep 1, 24, 26, 60, 99, 0 and 100 % of their elements,
+    each one to three tiles long and ragged, in turn: tiles that keep under a quarter of
+    their elements look back 32 status words per poll, the others 8, so both kinds of
+    look-back meet in one chain."""
+    rng = np.random.default_rng(2024)
+    fracs = [0.01, 0.24, 0.26, 0.6, 0.99, 0.0, 1.0]
+    parts = []
+    for i in range(70):
+        m = int(rng.integers(1, 4)) * TILE + int(rng.integers(0, 100))
+        keep = rng.random(m) < fracs[i % len(fracs)]
+        parts.append(np.where(keep, rng.integers(0, 1000, m), rng.integers(1000, 1 << 31, m)).astype(np.int32))
+    check_compact(np.concatenate(parts), "lt", np.int32(1000))
 
 
 def test_compact_unaligned_input():

@@ -11,9 +11,9 @@ from gpu_util import DEV, bits, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-TILE = 32768  # the library's compaction tile
+TILE = 16384  # the library's compaction tile
 SENTINEL = 0xDEADBEEF
-SIZES = [1, 2, 3, 17, 4095, 4096, 4097, 16383, 16385, TILE - 1, TILE, TILE + 1, 3 * TILE + 5, 300_007]
+SIZES = [1, 2, 3, 17, 4095, 4096, 4097, TILE - 1, TILE, TILE + 1, 2 * TILE - 1, 2 * TILE + 1, 3 * TILE + 5, 300_007]
 
 
 def flags_for(n, seed, p):
