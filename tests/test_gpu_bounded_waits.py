@@ -36,7 +36,7 @@ INT32, UINT32, F32 = 0, 1, 2
 SUM, MAX, AFFINE = 0, 1, 7
 LT, DETERMINISTIC, INCOMPLETE = 0, 3, 5
 N = 1 << 25            # hundreds of tiles: the ticket paths
-N_FALLBACK = (1 << 22) + 12345  # 158 scan tiles, 129 compaction tiles: the forced fallbacks
+N_FALLBACK = (1 << 22) + 12345  # 158 scan tiles, 257 compaction tiles: the forced fallbacks
 
 
 @pytest.fixture(scope="module")
