@@ -15,7 +15,7 @@ from gpu_util import DEV, bits, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 N = 40 * 26624 + 11      # the scan: 41 tiles, the last one ragged
-NC = 9 * 32768 + 5       # compaction: 10 tiles
+NC = 18 * 16384 + 5       # compaction: 19 tiles, the last one ragged
 
 
 def test_replays_match_eager_calls():
