@@ -13,7 +13,7 @@
 //      is kept, so the result is stable and unique;
 //   4. a control wave looks back over the tile status words for the number of
 //      elements kept by all earlier tiles (the tile's output offset), 8 words per
-//      poll, or 32 for a tile that keeps few elements;
+//      poll, or 32 for a tile that moves little data;
 //   5. the staged run is copied from LDS to out[offset ...] with consecutive
 //      lanes on consecutive addresses; the last tile writes the count.
 // Blocks are persistent and pipelined: the next tile's loads and count run while
@@ -37,10 +37,17 @@ constexpr int CP_THREADS = CP_BLOCK + 64;           // data waves + one control 
 constexpr int CP_CHUNKS = LS_CP_CHUNKS;             // 16-byte runs per data thread
 constexpr int CP_TILE = CP_BLOCK * CP_CHUNKS * 4;   // 16384 elements (64 KiB staged in LDS) by default
 constexpr int CP_LB_WIDE = 8;                       // status words per look-back poll
-// A tile that keeps fewer than a quarter of its elements polls 32 words at a time.
-// Measured on MI355X (int32, 2^27, 1 / 50 / 99 % kept): 109 / 137 / 178 us, against
-// 113 / 137 / 179 us with 8 words for every tile and 109 / 146 / 208 us with 32.
+// A tile that moves little data -- its loads plus 4 bytes per kept element under
+// CP_SPARSE_BYTES -- polls 32 words at a time: it reaches a published prefix in
+// fewer round trips, while for the others wide polls compete with the data stream.
+// Measured on MI355X, 2^27 elements: compact_if 109 / 118 / 137 / 178 us at 1 / 20 /
+// 50 / 99 % kept, against 113 / 120 / 137 / 179 us with 8 words for every tile (32
+// words for every tile: 146 / 208 us at 50 / 99 %); index selection by flags 103 /
+// 128 / 138 us at 50 / 80 / 98 %, against 117 / 130 / 138 us with 8 words.  A tile of
+// flags loads 16 KiB, so its cut falls at 87.5 % kept; a tile of values loads 64 KiB:
+// 12.5 %.
 constexpr int CP_LB_WIDE_SPARSE = 32;
+constexpr uint32_t CP_SPARSE_BYTES = 72 * 1024;
 
 // Predicate through a 4-entry truth table indexed by the comparison outcome:
 // 0 = greater, 1 = less, 2 = equal, 3 = unordered (a NaN is involved).
@@ -114,6 +121,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
     constexpr int PPL = (PARTS + 63) / 64;       // parts per lane in their scan
     constexpr uint32_t RUN_STRIDE = CP_BLOCK * 16u;
     constexpr bool LOAD_VALUES = (SRC == SRC_CMP) || (PAY == PAY_VALUE);
+    constexpr uint32_t TILE_LOAD_BYTES = (LOAD_VALUES ? 4u * CP_TILE : 0u) + (SRC == SRC_FLAGS ? uint32_t(CP_TILE) : 0u);
     static_assert(PARTS <= 64 * PPL, "the (run, wave) counts are scanned by one wave, PPL per lane");
     static_assert((CP_WAVES & (CP_WAVES - 1)) == 0, "arrival counting takes CP_WAVES a power of two");
     static_assert(CP_CHUNKS <= 16, "keep bits of all runs fit in 64 bits");
@@ -346,7 +354,7 @@ LS_CP_WAVES_ATTR __global__ __launch_bounds__(CP_THREADS) void compact_kernel(co
             // tiles, by look-back (missing counts recounted here when out of time)
             int64_t base = 0;
             if (cur != 0) {
-                base = kept < uint32_t(CP_TILE / 4)
+                base = TILE_LOAD_BYTES + 4u * kept < CP_SPARSE_BYTES
                            ? int64_t(lookback<CountCodec, CP_LB_WIDE_SPARSE>(status, cur, ep, hdr, recount))
                            : int64_t(lookback<CountCodec, CP_LB_WIDE>(status, cur, ep, hdr, recount));
                 if (lane == 0)
