@@ -441,7 +441,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "int32 exclusive sum scan, N=2^28, values U{0..15} (numpy PCG64)",
                    "n": h["n"], "scheme": "single pass, tile prefixes published by one chasing wave",
-                   "tile_elems": 26624},
+                   "tile_elems": 28672},
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": h["traffic"]},

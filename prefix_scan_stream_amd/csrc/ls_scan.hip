@@ -9,7 +9,7 @@
 // bound an HBM-limited scan:
 //   1. a block's tile is its block index (the fixed-order scheme instead takes
 //      the next tile id from a counter, in the order blocks start); it loads the
-//      tile (26624 elements; 16384 for the affine maps) with 128-bit loads;
+//      tile (28672 elements; 16384 for the affine maps) with 128-bit loads;
 //   2. it scans the tile in registers (serial runs of 4, DPP wave scan, one wave
 //      over the (run, wave) totals) and publishes the tile total;
 //   3. its first wave waits for the full prefix of the previous tile, which one
@@ -41,11 +41,12 @@ static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanne
 // The single pass uses 8-wave blocks.  A tile holds its data in registers until
 // its prefix is known, so the tile size sets how long the pipeline of resident
 // tiles takes to fill and drain (two blocks per CU: 512 tiles), against the
-// number of tiles the chasing wave must cover.  13 runs per thread (26624-element
-// tiles) measured best: 2^28 in 338-340 us, against 341-343 for 12 and 14 runs,
-// 345-348 for 16 (32768) and 351 for 8 (16384) (measured while tiles still took
-// their ids from a counter atomic; tiles by block index then took 13 runs from
-// 334 to 326 us).  The deterministic scheme keeps 16 runs: its fixed groups of 64
+// number of tiles the chasing wave must cover.  With tiles by block index, 14 runs
+// per thread (28672-element tiles) measured best: 2^28 in 322-323 us, against
+// 325-326 for 13 runs, 323-324 for 15, 334-336 for 16 and 346 / 377 for 10 / 8
+// (float32 sum of 2^26: 83.5-84, 84-84.5, 85, 87 and 90 / 94.5 us).  While tiles
+// took their ids from a counter atomic, 13 runs had been best (338-340 us against
+// 341-343 for 12 and 14).  The deterministic scheme keeps 16 runs: its fixed groups of 64
 // tiles are slower with smaller tiles (float32 2^26: 98 against 100-102 us).
 // 16-wave blocks with 65536-element tiles (one block per CU) were slower
 // (373-381 us).
@@ -55,10 +56,10 @@ static_assert(SCAN_WAVES * SCAN_CHUNKS <= 64, "the (run, wave) totals are scanne
 constexpr int SP_BLOCK = LS_SP_BLOCK;
 constexpr int SP_WAVES = SP_BLOCK / 64;
 #ifndef LS_SP_CHUNKS
-#define LS_SP_CHUNKS 13
+#define LS_SP_CHUNKS 14
 #endif
 constexpr int SP_CHUNKS = LS_SP_CHUNKS;
-constexpr int SP_TILE = SP_BLOCK * SP_CHUNKS * 4;          // 26624 elements
+constexpr int SP_TILE = SP_BLOCK * SP_CHUNKS * 4;          // 28672 elements
 constexpr int SP_FIXED_TILE = SP_BLOCK * SCAN_CHUNKS * 4;  // 32768 elements (deterministic)
 
 // Runs per thread of the single pass, by operator.  The affine maps' combine costs

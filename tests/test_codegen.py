@@ -72,7 +72,7 @@ def kernel_body(text, mangled_prefix):
 
 
 @pytest.mark.parametrize("src,prefix,runs", [
-    ("ls_scan.hip", "_ZN2ls23scan_single_pass_kernelINS_6SumU32ELb0ELb1ELi13ELb0E", 13),
+    ("ls_scan.hip", "_ZN2ls23scan_single_pass_kernelINS_6SumU32ELb0ELb1ELi14ELb0E", 14),
     ("ls_scan.hip", "_ZN2ls23scan_single_pass_kernelINS_6SumF32ELb0ELb1ELi16ELb1E", 16),
     ("ls_scan.hip", "_ZN2ls18tile_reduce_kernelINS_6SumU32ELb1E", 16),
     ("ls_scan.hip", "_ZN2ls16tile_scan_kernelINS_6SumU32ELb0ELb1E", 16),
@@ -81,7 +81,7 @@ def kernel_body(text, mangled_prefix):
 ])
 def test_aligned_tiles_load_128_bits(asm, src, prefix, runs):
     """Aligned tiles are read with 128-bit loads only (one per run of 4 elements; the
-    single pass has 13 runs per thread, its deterministic form 16)."""
+    single pass has 14 runs per thread, its deterministic form 16)."""
     body = kernel_body(asm[src], prefix)
     assert len(re.findall(r"buffer_load_dwordx4", body)) >= runs
     assert not re.search(r"buffer_load_dword\s", body)

@@ -14,7 +14,7 @@ from gpu_util import DEV, bits, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-N = 40 * 26624 + 11      # the scan: 41 tiles, the last one ragged
+N = 40 * 28672 + 11      # the scan: 41 tiles, the last one ragged
 NC = 18 * 16384 + 5       # compaction: 19 tiles, the last one ragged
 
 
@@ -75,8 +75,8 @@ def test_earlier_graph_survives_a_larger_capture():
     """Two captures on the same (default capture) stream, the second larger: the
     binding grows that stream's workspace for the second but keeps the first
     graph's, so replaying the first after the second still matches eager calls."""
-    small = to_dev(wl.int_uniform(3 * 26624 + 5, 0, 16, seed=960))
-    big = to_dev(wl.int_uniform(700 * 26624 + 7, 0, 16, seed=961))
+    small = to_dev(wl.int_uniform(3 * 28672 + 5, 0, 16, seed=960))
+    big = to_dev(wl.int_uniform(700 * 28672 + 7, 0, 16, seed=961))
     want_s = to_host(ps.scan_exclusive(small, "sum"))
     want_b = to_host(ps.scan_exclusive(big, "sum"))
     ys, yb = torch.empty_like(small), torch.empty_like(big)

@@ -20,7 +20,7 @@ from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 pytestmark = pytest.mark.gpu
 
 TILE = 16384     # the three-phase schemes' tile; the deterministic single pass's is 2 * TILE
-SP_TILE = 26624  # the single pass's tile
+SP_TILE = 28672  # the single pass's tile
 SIZES = [1, 2, 3, 63, 64, 65, 1023, 4096, 4097, TILE - 1, TILE, TILE + 1, 2 * TILE - 1, 2 * TILE + 1,
          3 * TILE + 7, 70 * TILE + 5, 300_003, SP_TILE - 1, SP_TILE + 1, 2 * SP_TILE + 1,
          66 * SP_TILE + 3]

@@ -16,7 +16,7 @@ from gpu_util import DEV, bits, to_dev, to_host, ws_error_word
 pytestmark = pytest.mark.gpu
 
 TILE = 8192      # a quarter of the deterministic single pass's tile (32768)
-SP_TILE = 26624  # the single pass's tile; the chasing wave reads 64 tiles per poll
+SP_TILE = 28672  # the single pass's tile; the chasing wave reads 64 tiles per poll
 SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 1023, 4095, 4096, 4097, TILE - 1, TILE, TILE + 1,
          2 * TILE - 1, 2 * TILE + 1, 4 * TILE - 1, 4 * TILE, 4 * TILE + 1,
          3 * TILE + 7, 64 * TILE, 257 * TILE + 5, 300_003, 600 * TILE + 3,

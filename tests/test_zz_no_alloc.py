@@ -16,7 +16,7 @@ from gpu_util import DEV, bits, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-SP_TILE = 26624
+SP_TILE = 28672
 CASES = [("int32", "sum"), ("uint32", "xor"), ("int32", "max"), ("float32", "sum"),
          ("float32", "max"), ("uint32", "affine")]
 # (first n, second n): several tiles and a ragged tail, then fewer tiles
